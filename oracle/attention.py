@@ -1,0 +1,136 @@
+"""Paged GQA attention, written out from its definition in fp64 (test infrastructure).
+
+What is computed (the masked SDPA that the AstrAI pages describe):
+
+* [attention.py @c9ceca1], the commit that batches the torch-native path into one
+  masked SDPA call: per request b, query row i sits at absolute position
+  c_b + i with c_b = seq_len_b - q_len_b; key t is visible to row i iff
+  t <= c_b + i; masked keys get a weight of exactly zero; outputs come back in
+  flat qo_indptr order.
+* [extension @6f67ba8], the commit wiring paged decode into the CUDA backend:
+  K/V of position t of request b live in pool slot req_to_token[row_b + t]
+  (a page table with page size one); kv_indptr is the prefix sum of seq_lens;
+  decode is always causal, i.e. the single query sees all seq_len keys.
+* [extension @6f67ba8], the commit adding the torch fallback with GQA head
+  expansion: query head h reads kv head floor(h / (Hq / Hkv)) (repeat-interleave
+  reading; the alternative h mod Hkv is not used).
+
+Precision: bf16 inputs are widened exactly to fp64; sm_scale is first rounded to
+fp32 (the precision the library receives it in), then widened.  Everything
+else is fp64.  Output rounding is not part of the definition: callers compare
+the fp64 result with the bf16 output under a tolerance.
+
+Parity: pinned (tests/test_oracle.py) by closed forms (one key returns V
+exactly; identical keys or a zero query return the mean of V; two keys give
+sigmoid weights), torch's fp64 scaled_dot_product_attention on the gathered
+keys, a brute-force loop on tiny inputs, slot-permutation invariance and the
+hand-derived fixtures in tests/golden/.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """Exact widening of bf16 bit patterns (uint16) to float64."""
+    b = np.asarray(bits, dtype=np.uint16)
+    with np.errstate(invalid="ignore"):
+        return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16_bits(x) -> np.ndarray:
+    """Round float64 values to bf16 with round-to-nearest-even, returning uint16 bits.
+
+    Rounds once, directly from fp64 (no intermediate fp32 rounding): the value is
+    scaled by its bf16 quantum (2^(e-7), floored at the subnormal quantum
+    2^-133), rounded to the nearest integer with ties to even, and scaled back.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    finite = np.isfinite(x)
+    xf = np.where(finite, x, 0.0)
+    _, e = np.frexp(xf)            # xf = m * 2^e with 0.5 <= |m| < 1, so 2^(e-1) <= |xf|
+    e = np.maximum(e - 1, -126)     # unbiased exponent, clamped to the normal minimum
+    quantum = np.ldexp(1.0, e - 7)
+    r = np.rint(xf / quantum) * quantum   # np.rint rounds half to even
+    r32 = r.astype(np.float32)            # exact: r has <= 8 significant bits (or is inf)
+    bits = (r32.view(np.uint32) >> 16).astype(np.uint16)
+    out[...] = bits
+    out[np.isnan(x)] = 0x7FC0
+    out[np.isposinf(x)] = 0x7F80
+    out[np.isneginf(x)] = 0xFF80
+    return out
+
+
+def request_slots(req_to_token, req_to_token_stride, kv_indptr, b) -> np.ndarray:
+    """Pool slots of request b's positions 0..L_b-1.
+
+    Row base is b * stride for a 2-D table, or kv_indptr[b] for a flat table
+    (stride 0).  Page size is one: position t maps to exactly one slot.
+    """
+    L = int(kv_indptr[b + 1]) - int(kv_indptr[b])
+    base = b * int(req_to_token_stride) if req_to_token_stride > 0 else int(kv_indptr[b])
+    return np.asarray(req_to_token[base: base + L], dtype=np.int64)
+
+
+def attention_over_range(qf, kf, vf, sigma, visible):
+    """Masked softmax attention for one head.
+
+    qf [R, D], kf [T, D], vf [T, D] float64; visible [R, T] bool.
+    Returns (o [R, D], m [R], l [R]) where m is the row max of the visible
+    scaled logits, l = sum of exp(s - m) over visible keys, and
+    o = sum exp(s - m) v / l.  Rows with no visible key are not allowed.
+    """
+    s = sigma * (qf @ kf.T)
+    s_vis = np.where(visible, s, -np.inf)
+    m = s_vis.max(axis=1)
+    if not np.all(np.isfinite(m)):
+        raise ValueError("a row has no visible key")
+    p = np.where(visible, np.exp(s_vis - m[:, None]), 0.0)
+    l = p.sum(axis=1)
+    o = (p @ vf) / l[:, None]
+    return o, m, l
+
+
+def paged_attention(q_bits, k_pool_bits, v_pool_bits, req_to_token, req_to_token_stride,
+                    kv_indptr, sm_scale, qo_indptr=None):
+    """Reference paged GQA attention.
+
+    q_bits: [rows, Hq, D] bf16 bits; rows = B for decode (qo_indptr None) or
+    qo_indptr[B] for prefill, in flat qo_indptr order.
+    k_pool_bits, v_pool_bits: [num_slots, Hkv, D] bf16 bits.
+    Returns (o [rows, Hq, D] float64, lse [rows, Hq] float64 natural log).
+    Requires 1 <= q_len_b <= seq_len_b for every request.
+    """
+    q_bits = np.asarray(q_bits)
+    rows, Hq, D = q_bits.shape
+    Hkv = k_pool_bits.shape[1]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    group = Hq // Hkv
+    sigma = float(np.float32(sm_scale))
+    kv_indptr = np.asarray(kv_indptr, dtype=np.int64)
+    B = kv_indptr.shape[0] - 1
+    out = np.zeros((rows, Hq, D), dtype=np.float64)
+    lse = np.zeros((rows, Hq), dtype=np.float64)
+    for b in range(B):
+        L = int(kv_indptr[b + 1] - kv_indptr[b])
+        if qo_indptr is None:
+            row0, qb = b, 1
+        else:
+            row0 = int(qo_indptr[b])
+            qb = int(qo_indptr[b + 1]) - row0
+        if not (1 <= qb <= L):
+            raise ValueError(f"request {b}: need 1 <= q_len ({qb}) <= seq_len ({L})")
+        c = L - qb  # absolute position of the first query row
+        slots = request_slots(req_to_token, req_to_token_stride, kv_indptr, b)
+        K = bf16_bits_to_f64(k_pool_bits[slots])   # [L, Hkv, D]
+        V = bf16_bits_to_f64(v_pool_bits[slots])
+        Q = bf16_bits_to_f64(q_bits[row0: row0 + qb])  # [qb, Hq, D]
+        visible = np.arange(L)[None, :] <= (c + np.arange(qb))[:, None]
+        for h in range(Hq):
+            g = h // group
+            o, m, l = attention_over_range(Q[:, h, :], K[:, g, :], V[:, g, :], sigma, visible)
+            out[row0: row0 + qb, h] = o
+            lse[row0: row0 + qb, h] = m + np.log(l)
+    return out, lse

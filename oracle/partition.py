@@ -1,0 +1,161 @@
+"""Split-KV decode: work partition, per-split partials and their log-sum-exp merge (fp64).
+
+Test infrastructure.  This is an independent statement of the split planner,
+of what each split's partial holds, and of the combine step, so that the
+library's plan and its workspace contents can be checked exactly.
+
+The pages fix only the shape of the method, not the plan:
+* [extension @6f67ba8], the commit moving decode onto split-KV: each split
+  writes an output partial (o_part) and a (max, sum) partial (ml_part), and a
+  separate combine kernel merges the splits into the final output.
+* [extension @6f67ba8], the commit extracting shared helpers, which names a
+  compute_num_splits helper without giving its rule.
+* [extension @6f67ba8], the commit dropping the partial memset: every slot a
+  split owns is written, so unowned slots are never read.
+
+The rule below is this project's reading (the pages leave it open):
+
+Balanced flat partition.  Let N = kv_indptr[B] be the total number of keys.
+The keys of one kv head are laid end to end in request order and cut into
+W = min(Wh, N) contiguous ranges of near-equal length: work group w
+(0 <= w < W) takes flat positions [floor(w*N/W), floor((w+1)*N/W)), which
+holds at least one key; work groups w >= W (possible when a fixed Wh exceeds
+the key count) do nothing.  A range cut by request
+boundaries yields one *piece* per request it touches; piece (w, b) writes
+partial slot w + b.  Consecutive pieces advance w, b or both, so slots are
+unique and lie in [0, W + B - 1), within the Wh + B - 1 slots the workspace
+holds.  Request b's pieces are the work groups w_first(b)..w_last(b), all
+non-empty, where the work group holding flat position x is
+ceil((x + 1) * W / N) - 1.
+
+Planner (integers only): Wh = forced value if given, else
+min(ceil(WG_PER_CU * num_cus / Hkv), max(1, ceil(N / MIN_TOKENS)), MAX_SPLITS),
+and at least 1.
+
+Partial of one piece and query head: m = max of the scaled logits over the
+piece's keys, l = sum exp(s - m), o = sum exp(s - m) v / l (normalised).
+Merge: M = max m_s, w_s = l_s exp(m_s - M), O = sum w_s o_s / sum w_s,
+lse = M + ln sum w_s.
+
+Parity: pinned in tests/test_oracle.py -- the merge of split partials equals
+the direct definition (oracle.attention) to 1e-12 for every split count,
+pieces tile each request exactly, slots are unique, ranges differ by at most
+one key, the closed-form work-group lookup matches the table, and a
+hand-worked partition fixture in tests/golden/.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .attention import attention_over_range, bf16_bits_to_f64, request_slots
+
+DEFAULTS = {
+    "wg_per_cu": 2,        # work groups per compute unit the plan aims for
+    "min_tokens": 64,      # fewest keys per work group on average
+    "max_splits": 256,     # cap on work groups per kv head
+}
+
+
+def _ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def plan_num_splits(kv_indptr, num_kv_heads, num_cus, forced=0, **consts):
+    """Work groups per kv head (Wh) for a decode batch."""
+    c = dict(DEFAULTS)
+    c.update(consts)
+    if forced and forced > 0:
+        return int(forced)
+    N = int(kv_indptr[-1])
+    target = _ceil_div(c["wg_per_cu"] * int(num_cus), int(num_kv_heads))
+    by_len = max(1, _ceil_div(N, c["min_tokens"]))
+    return max(1, min(target, by_len, c["max_splits"]))
+
+
+def active_groups(N: int, Wh: int) -> int:
+    """Work groups that hold keys: min(Wh, N)."""
+    return min(int(Wh), int(N))
+
+
+def wg_bounds(N: int, Wh: int, w: int):
+    """Flat key range [lo, hi) of work group w (empty for w >= min(Wh, N))."""
+    W = active_groups(N, Wh)
+    if w >= W:
+        return N, N
+    return (w * N) // W, ((w + 1) * N) // W
+
+
+def piece_table(kv_indptr, Wh: int):
+    """All pieces as (w, b, t_begin, t_end, slot); t_* are positions inside request b."""
+    kv = [int(x) for x in kv_indptr]
+    B = len(kv) - 1
+    N = kv[-1]
+    pieces = []
+    for w in range(Wh):
+        lo, hi = wg_bounds(N, Wh, w)
+        for b in range(B):
+            a = max(lo, kv[b])
+            e = min(hi, kv[b + 1])
+            if a < e:
+                pieces.append((w, b, a - kv[b], e - kv[b], w + b))
+    return pieces
+
+
+def pieces_of_request(kv_indptr, Wh: int, b: int):
+    """(w_first, w_last) of request b, from the closed-form lookup."""
+    N = int(kv_indptr[-1])
+    W = active_groups(N, Wh)
+    x0 = int(kv_indptr[b])
+    x1 = int(kv_indptr[b + 1]) - 1
+    return _ceil_div((x0 + 1) * W, N) - 1, _ceil_div((x1 + 1) * W, N) - 1
+
+
+def split_partials(q_bits, k_pool_bits, v_pool_bits, req_to_token, req_to_token_stride,
+                   kv_indptr, sm_scale, Wh):
+    """Per-piece partials. Returns (o_part [Hq, P, D], ml_part [Hq, P, 2]); unwritten slots are NaN."""
+    q_bits = np.asarray(q_bits)
+    B, Hq, D = q_bits.shape
+    Hkv = k_pool_bits.shape[1]
+    group = Hq // Hkv
+    sigma = float(np.float32(sm_scale))
+    P = Wh + B - 1
+    o_part = np.full((Hq, P, D), np.nan)
+    ml_part = np.full((Hq, P, 2), np.nan)
+    for (w, b, t0, t1, slot) in piece_table(kv_indptr, Wh):
+        slots = request_slots(req_to_token, req_to_token_stride, kv_indptr, b)[t0:t1]
+        K = bf16_bits_to_f64(k_pool_bits[slots])
+        V = bf16_bits_to_f64(v_pool_bits[slots])
+        Q = bf16_bits_to_f64(q_bits[b])
+        vis = np.ones((1, t1 - t0), dtype=bool)
+        for h in range(Hq):
+            g = h // group
+            o, m, l = attention_over_range(Q[h][None, :], K[:, g, :], V[:, g, :], sigma, vis)
+            o_part[h, slot] = o[0]
+            ml_part[h, slot] = (m[0], l[0])
+    return o_part, ml_part
+
+
+def combine_partials(o_part, ml_part, kv_indptr, Wh):
+    """Log-sum-exp merge of each request's pieces. Returns (o [B, Hq, D], lse [B, Hq])."""
+    Hq, _, D = o_part.shape
+    B = len(kv_indptr) - 1
+    out = np.zeros((B, Hq, D))
+    lse = np.zeros((B, Hq))
+    for b in range(B):
+        wf, wl = pieces_of_request(kv_indptr, Wh, b)
+        sl = np.arange(wf, wl + 1) + b
+        m = ml_part[:, sl, 0]       # [Hq, n]
+        l = ml_part[:, sl, 1]
+        M = m.max(axis=1)
+        wgt = l * np.exp(m - M[:, None])
+        tot = wgt.sum(axis=1)
+        out[b] = np.einsum("hs,hsd->hd", wgt, o_part[:, sl, :]) / tot[:, None]
+        lse[b] = M + np.log(tot)
+    return out, lse
+
+
+def decode_via_splits(q_bits, k_pool_bits, v_pool_bits, req_to_token, req_to_token_stride,
+                      kv_indptr, sm_scale, Wh):
+    o_part, ml_part = split_partials(q_bits, k_pool_bits, v_pool_bits, req_to_token,
+                                     req_to_token_stride, kv_indptr, sm_scale, Wh)
+    return combine_partials(o_part, ml_part, kv_indptr, Wh)
