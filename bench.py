@@ -1,0 +1,281 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged GQA decode path on one MI355X.
+
+One step = one astr_paged_decode call (split kernel + combine kernel) over one
+batch of the decode microbench shape: B=32 requests, 1 query token each,
+Hq=32, Hkv=8, head_dim=128, bf16, seq_len ~ U{200..2000}, a 2^17-slot pool
+addressed through a random-permutation req_to_token (page size 1).
+
+Caches are kept cold: the timed steps rotate over --sets independent input
+sets (pools, tables, queries), so the bytes one step touches are gone from
+the 256 MB Infinity Cache by the time that set comes round again.  Inputs
+are resident in HBM before the timed region starts.
+
+Prints one JSON line (stdout).  `value` is algorithmic HBM bytes of the whole
+call (K + V + Q + O + index arrays + lse) per second, in GB/s.  `roofline`
+is for the dominant kernel (the split kernel), timed live with HIP events the
+library records around each kernel on the launch stream.  `cpu_baseline`
+times the fp64 CPU oracle on the same workload.  `prefill` reports the ragged
+prefill kernel (B=8, prefix U{0..2048}, q_len U{1..512}) against the bf16
+MFMA peak.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "paged GQA decode µs/call + achieved HBM GB/s (% peak), B=32 seq 200-2000"
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, AMD published peak
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, AMD published peak
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def decode_bytes(inp, with_lse=True):
+    """Algorithmic bytes of one decode call, counted once."""
+    B, Hq, D = inp["q"].shape
+    Hkv = inp["num_kv_heads"]
+    N = int(inp["kv_indptr"][-1])
+    kv = N * Hkv * D * 2 * 2
+    qo = 2 * B * Hq * D * 2
+    idx = N * 4 + (B + 1) * 4
+    return kv + qo + idx + (B * Hq * 4 if with_lse else 0)
+
+
+def split_kernel_bytes(inp):
+    """Bytes the split kernel must read: K + V + Q + req_to_token entries + kv_indptr."""
+    B, Hq, D = inp["q"].shape
+    Hkv = inp["num_kv_heads"]
+    N = int(inp["kv_indptr"][-1])
+    return N * Hkv * D * 2 * 2 + B * Hq * D * 2 + N * 4 + (B + 1) * 4
+
+
+def prefill_flops(inp):
+    """4 * D * Hq per visible (query row, key) pair; causally masked pairs are not counted."""
+    _, Hq, D = inp["q"].shape
+    kv, qo = inp["kv_indptr"], inp["qo_indptr"]
+    pairs = 0
+    for b in range(len(kv) - 1):
+        L = int(kv[b + 1] - kv[b])
+        qb = int(qo[b + 1] - qo[b])
+        c = L - qb
+        pairs += qb * c + qb * (qb + 1) // 2
+    return 4 * D * Hq * pairs
+
+
+def read_traffic(kernel_key):
+    """HBM traffic per launch from a committed rocprofv3 PMC summary, if it is for the current source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel_key}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    src = os.path.join(ROOT, rec["source"])
+    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, budget_s):
+    import oracle
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        runs, t0 = 0, time.perf_counter()
+        while True:
+            out = oracle.paged_attention(inp["q"], inp["k_pool"], inp["v_pool"], inp["req_to_token"],
+                                         inp["req_to_token_stride"], inp["kv_indptr"], inp["sm_scale"])
+            runs += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                break
+    per = el / runs
+    return out, {"value": decode_bytes(inp) / per / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                 "sample": f"fp64 NumPy oracle over one full decode_b32 batch (set 0, {B_str(inp)}), "
+                           f"{runs} run(s) in {el:.1f} s, {per * 1e3:.1f} ms/call, BLAS limited to 1 thread; "
+                           f"host has {len(os.sched_getaffinity(0))} cores"}
+
+
+def B_str(inp):
+    return f"B={inp['q'].shape[0]}, {int(inp['kv_indptr'][-1])} keys"
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--sets", type=int, default=4, help="independent input sets rotated to keep caches cold")
+    ap.add_argument("--config", default="decode_b32", help="decode workload (tiny, decode_b32, long_b1, long_b4, ragged_b256)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget (0 = skip)")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--probe", action="store_true", help="also measure torch copy / row-gather bandwidth ceilings")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (this path has no "
+              "multi-GPU mode)", file=sys.stderr)
+        return 2
+
+    import torch
+    from paged_gqa_decode_astr_amd import _lib, tensors
+    from paged_gqa_decode_astr_amd.workloads import CONFIGS, make_inputs
+
+    _lib.load_library()
+    dev = "cuda"
+    cfg = CONFIGS[args.config]
+    log(f"[bench] building {args.sets} input sets of {args.config}")
+    sets = []
+    for t in range(args.sets):
+        inp = make_inputs(args.config, t)
+        d = tensors.to_device(inp, dev)
+        B, Hq, D = inp["q"].shape
+        d["o"] = torch.empty(B, Hq, D, dtype=torch.bfloat16, device=dev)
+        d["lse"] = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+        d["ws"] = tensors.decode_workspace(B, Hq, D, dev)
+        sets.append((inp, d))
+    torch.cuda.synchronize()
+
+    def step(k, events=None):
+        _, d = sets[k % len(sets)]
+        tensors.run_decode(d, o=d["o"], lse=d["lse"], workspace=d["ws"], timing_events=events)
+
+    log(f"[bench] warmup {args.warmup}")
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+
+    log(f"[bench] timing {args.steps} steps")
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for k in range(args.steps):
+        step(k)
+    stop.record()
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(stop)
+    ms_per_step = ms_total / args.steps
+    total_bytes = sum(decode_bytes(sets[k % len(sets)][0]) for k in range(args.steps))
+    value = total_bytes / (ms_total * 1e-3) / 1e9
+
+    # Per-kernel durations: events recorded by the library around each kernel, same stream.
+    log("[bench] per-kernel event timing")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        step(k, evs[k])
+    torch.cuda.synchronize()
+    split_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    comb_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    split_bytes = sum(split_kernel_bytes(sets[k % len(sets)][0]) for k in range(args.steps))
+    achieved = split_bytes / (split_ms.sum() * 1e-3) / 1e9
+    plan = _lib.astr_plan_decode(_lib.make_args(
+        sets[0][1]["q"], sets[0][1]["k_pool"], sets[0][1]["v_pool"], sets[0][1]["req_to_token"],
+        sets[0][1]["kv_indptr"], sets[0][1]["kv_indptr_host"], sets[0][1]["o"], sm_scale=1.0,
+        req_to_token_stride=sets[0][1]["req_to_token_stride"])[0], 0)
+
+    B, Hq, D = sets[0][0]["q"].shape
+    G = Hq // cfg.num_kv_heads
+    kernel_name = f"decode_split_kernel<{D},{G}>"
+    traffic = read_traffic(f"decode_split_{args.config}")
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{args.config}: {cfg.description}; B={B} Hq={Hq} Hkv={cfg.num_kv_heads} D={D}, "
+                               f"pool 2^{int(math.log2(cfg.num_slots))} slots, page_size 1",
+                   "batch": B, "cache": f"cold: {args.sets} rotating input sets",
+                   "num_splits": plan.num_splits},
+        "us_per_call": round(ms_per_step * 1e3, 2),
+        "pct_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
+        "kernels_us": {"split": round(float(split_ms.mean()) * 1e3, 2), "combine": round(float(comb_ms.mean()) * 1e3, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic, "kernel": kernel_name,
+                     "bytes_per_launch": int(split_bytes / args.steps),
+                     "us_per_launch": round(float(split_ms.mean()) * 1e3, 2)},
+    }
+
+    if not args.no_prefill:
+        log("[bench] prefill leg")
+        pin = make_inputs("prefill_b8", 0)
+        pd = tensors.to_device(pin, dev)
+        po = torch.empty_like(pd["q"])
+        plse = torch.empty(pd["q"].shape[0], pd["q"].shape[1], dtype=torch.float32, device=dev)
+        for _ in range(5):
+            tensors.run_prefill(pd, o=po, lse=plse)
+        torch.cuda.synchronize()
+        psteps = max(10, args.steps // 4)
+        pev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(psteps)]
+        for k in range(psteps):
+            tensors.run_prefill(pd, o=po, lse=plse, timing_events=pev[k] + [None])
+        torch.cuda.synchronize()
+        pms = float(np.mean([e[0].elapsed_time(e[1]) for e in pev]))
+        fl = prefill_flops(pin)
+        tf = fl / (pms * 1e-3) / 1e12
+        out["prefill"] = {"workload": f"prefill_b8: {CONFIGS['prefill_b8'].description}",
+                          "us_per_call": round(pms * 1e3, 2), "flops": fl,
+                          "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                                       "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                                       "kernel": f"prefill_kernel<{D},{G}>"}}
+
+    if args.probe:
+        log("[bench] probes")
+        n = 1 << 29
+        a = torch.empty(n, dtype=torch.int16, device=dev)
+        bb = torch.empty_like(a)
+        for _ in range(3):
+            bb.copy_(a)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(20):
+            bb.copy_(a)
+        t1.record()
+        torch.cuda.synchronize()
+        copy_gbs = 20 * 2 * a.numel() * 2 / (t0.elapsed_time(t1) * 1e-3) / 1e9
+        inp0, d0 = sets[0]
+        N = int(inp0["kv_indptr"][-1])
+        slots = torch.from_numpy(inp0["req_to_token"][inp0["req_to_token"] >= 0].astype(np.int64)).to(dev)
+        kf = d0["k_pool"].view(d0["k_pool"].shape[0], -1)
+        vf = d0["v_pool"].view(d0["v_pool"].shape[0], -1)
+        gk = torch.index_select(kf, 0, slots)
+        gv = torch.index_select(vf, 0, slots)
+        torch.cuda.synchronize()
+        t0.record()
+        for k in range(20):
+            _, dk = sets[k % len(sets)]
+            torch.index_select(dk["k_pool"].view(dk["k_pool"].shape[0], -1), 0, slots, out=gk)
+            torch.index_select(dk["v_pool"].view(dk["v_pool"].shape[0], -1), 0, slots, out=gv)
+        t1.record()
+        torch.cuda.synchronize()
+        gather_gbs = 20 * 2 * (2 * N * kf.shape[1] * 2) / (t0.elapsed_time(t1) * 1e-3) / 1e9
+        out["probes"] = {"torch_copy_GBs": round(copy_gbs, 1),
+                         "torch_row_gather_GBs": round(gather_gbs, 1),
+                         "note": "copy: read+write bytes of a 1 GiB device copy; gather: index_select of the same "
+                                 "2 KiB K and V slot rows (read + write counted)"}
+
+    if args.cpu_seconds > 0:
+        log("[bench] cpu oracle baseline")
+        inp0, d0 = sets[0]
+        step(0)
+        torch.cuda.synchronize()
+        (ref_o, ref_lse), cpu = cpu_baseline(inp0, args.cpu_seconds)
+        got = tensors.bf16_to_f64(d0["o"])
+        cpu["parity_max_abs"] = float(np.abs(got - ref_o).max())
+        out["cpu_baseline"] = cpu
+
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

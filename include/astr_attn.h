@@ -1,0 +1,177 @@
+/*
+ * astr_attn.h -- C ABI of the paged grouped-query attention library (gfx950).
+ *
+ * What the calls compute (AstrAI commit-list pages):
+ *  - [extension @6f67ba8] (commits page for astrai/extension at 6f67ba8), the
+ *    commit wiring paged decode into the CUDA backend: the K/V of position t of
+ *    request b sit in pool slot req_to_token[row_b + t] -- a page table with a
+ *    page size of one -- and decode is always causal (the single query of a
+ *    request sees all of its seq_len keys).
+ *  - [extension @6f67ba8], the commit that builds kv_indptr (prefix sum of
+ *    seq_lens) once per step, and the one hoisting qo_indptr for prefill.
+ *  - [attention.py @c9ceca1] (commits page for
+ *    astrai/extension/backend/attention.py at c9ceca1), the commit batching the
+ *    torch path: prefill query row i of request b sits at absolute position
+ *    seq_len_b - q_len_b + i and sees keys 0 .. that position; masked keys weigh
+ *    exactly zero; rows are stored in flat qo_indptr order.
+ *  - [extension @6f67ba8], the fallback commit with GQA head expansion: query
+ *    head h reads kv head h / (Hq / Hkv).
+ *  - [extension @6f67ba8], the split-KV commits: decode writes per-split
+ *    partials (o_part, ml_part) that a separate combine kernel merges; the
+ *    partials live in a caller-owned, preallocated workspace (the workspace
+ *    commit) and are written without a memset.
+ *
+ * Per request b and query head h (g = h / (Hq / Hkv), sigma = sm_scale):
+ *     s_t   = sigma * <q[row, h, :], K[slot_b(t), g, :]>      for visible t
+ *     O     = sum_t exp(s_t - m) V[slot_b(t), g, :] / sum_t exp(s_t - m)
+ *     lse   = m + ln sum_t exp(s_t - m)                       (m = max_t s_t)
+ * computed from bf16 inputs with fp32 accumulation; O is stored as bf16
+ * (round to nearest even), lse as fp32.
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers unless the name ends in _host.  bf16 data is
+ *    passed as its 16-bit storage.  Strides count elements, not bytes.
+ *  - The innermost (head_dim) dimension of q, o and the pools is contiguous.
+ *    q, o, k_pool, v_pool must be 16-byte aligned and their token/slot/head
+ *    strides multiples of 8 elements.
+ *  - Ownership: the caller owns every buffer (q, o, lse, pools, index arrays,
+ *    workspace).  The library never allocates or frees device memory, never
+ *    synchronises the device, never copies host->device and keeps no pointer
+ *    after a call returns.  *_host arrays are read only during the call.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *    null stream).  With a fixed plan (num_splits / max_q_len set) the enqueued
+ *    work reads lengths only from device memory, so a call can be captured into
+ *    a hip graph and replayed after the device index arrays change (same batch
+ *    size).  Concurrent calls need distinct workspaces.
+ *  - Errors: every argument is validated on the host before anything is
+ *    launched; on failure nothing is enqueued and the call returns a non-zero
+ *    astr_status whose message astr_last_error() gives (thread-local).  After
+ *    each launch hipGetLastError() is checked (ASTR_ERR_HIP).  No C++ exception
+ *    crosses this interface.  There is no fallback path.
+ *  - Caller contract not checked on the host (undefined behaviour if broken):
+ *    device index arrays hold the same values as their _host copies; every
+ *    slot id a request uses is in [0, num_slots); pools hold finite values at
+ *    the slots in use.  Slots no request uses are never read.
+ */
+#ifndef ASTR_ATTN_H
+#define ASTR_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ASTR_ABI_VERSION 1
+
+/* Default cap on work groups per kv head in an automatic decode plan. */
+#define ASTR_DEFAULT_MAX_SPLITS 256
+
+typedef enum astr_status {
+  ASTR_OK = 0,
+  ASTR_ERR_INVALID_ARG = 1,   /* malformed argument: null pointer, bad length, misalignment */
+  ASTR_ERR_UNSUPPORTED = 2,   /* well-formed but not built: head_dim or group size */
+  ASTR_ERR_WORKSPACE = 3,     /* workspace missing or smaller than the plan needs */
+  ASTR_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
+} astr_status;
+
+typedef struct astr_paged_args {
+  int32_t batch;          /* B >= 0 requests; B == 0 is a no-op */
+  int32_t num_qo_heads;   /* Hq >= 1 */
+  int32_t num_kv_heads;   /* Hkv >= 1, Hq % Hkv == 0, Hq / Hkv in {1, 2, 4, 8} */
+  int32_t head_dim;       /* D in {64, 128} */
+  float sm_scale;         /* logit scale, e.g. 1/sqrt(D) */
+
+  /* Queries, bf16.  Decode: row b is request b's query.  Prefill: rows in flat
+   * qo_indptr order (row qo_indptr[b] + i is request b's i-th new token).
+   * Element (row, h, d) at q[row * q_stride_tok + h * q_stride_head + d]. */
+  const void* q;
+  int64_t q_stride_tok, q_stride_head;
+  /* Output, bf16, same row convention and indexing as q. */
+  void* o;
+  int64_t o_stride_tok, o_stride_head;
+  /* Optional log-sum-exp (natural log), fp32: lse[row * lse_stride_tok + h].
+   * NULL skips it. */
+  float* lse;
+  int64_t lse_stride_tok;
+
+  /* KV pools, bf16: element (slot, g, d) at pool[slot * kv_stride_slot +
+   * g * kv_stride_head + d], slot in [0, num_slots). */
+  const void* k_pool;
+  const void* v_pool;
+  int64_t kv_stride_slot, kv_stride_head;
+  int64_t num_slots;
+
+  /* Page table, int32: slot of position t of request b is
+   * req_to_token[row_b + t] with row_b = b * req_to_token_stride, or
+   * row_b = kv_indptr[b] when req_to_token_stride == 0 (one flat list). */
+  const int32_t* req_to_token;
+  int64_t req_to_token_stride;
+
+  /* kv_indptr[B+1]: prefix sum of seq_lens, kv_indptr[0] == 0, every
+   * seq_len >= 1.  Both the device array and a host copy are required. */
+  const int32_t* kv_indptr;
+  const int32_t* kv_indptr_host;
+  /* Prefill only (NULL for decode): qo_indptr[B+1], prefix sum of q_lens,
+   * qo_indptr[0] == 0, 1 <= q_len_b <= seq_len_b. */
+  const int32_t* qo_indptr;
+  const int32_t* qo_indptr_host;
+
+  /* Decode plan: work groups per kv head.  0 = choose from kv_indptr_host and
+   * the device's CU count; > 0 fixes it (fixed grid, e.g. for graph capture). */
+  int32_t num_splits;
+  /* Prefill grid: 0 = max q_len from qo_indptr_host; > 0 fixes the grid's
+   * query-tile count for q_len up to this value (graph capture). */
+  int32_t max_q_len;
+
+  /* Optional timing hook: NULL, or an array of hipEvent_t the call records on
+   * `stream`.  Decode records [0] before the split kernel, [1] between the
+   * split and combine kernels, [2] after the combine kernel.  Prefill records
+   * [0] before and [1] after its kernel.  Elements may be NULL (skipped). */
+  void* const* timing_events;
+} astr_paged_args;
+
+typedef struct astr_decode_plan {
+  int32_t num_splits;      /* Wh: work groups per kv head */
+  int32_t num_partials;    /* partial slots per query head = Wh + B - 1 */
+  int32_t grid_x, grid_y, grid_z;  /* split-kernel grid: (Wh, Hkv, 1) */
+  int64_t workspace_bytes; /* workspace this plan needs */
+} astr_decode_plan;
+
+/* Workspace bytes a decode call needs for `batch` requests with up to
+ * `max_splits` work groups per kv head (0 = ASTR_DEFAULT_MAX_SPLITS).
+ * Layout (both fp32, offsets from the workspace base, P = Wh + B - 1):
+ *   o_part  at 0:                          [Hq][P][D]  normalised split output
+ *   ml_part at align256(Hq * P * D * 4):   [Hq][P][2]  (max logit m, sum l)
+ * m is in natural-log units of the scaled logits; l = sum exp(s - m).
+ * Returns 0 for invalid sizes.  Prefill needs no workspace. */
+size_t astr_workspace_size(int32_t batch, int32_t num_qo_heads, int32_t head_dim, int32_t max_splits);
+
+/* Host-only decode plan (no HIP call): the number of work groups per kv head
+ * and the workspace it needs.  num_cus > 0 sets the compute-unit count the
+ * plan targets; num_cus <= 0 asks the current device.  Needs kv_indptr_host
+ * unless a->num_splits > 0.  Returns astr_status. */
+int astr_plan_decode(const astr_paged_args* a, int32_t num_cus, astr_decode_plan* out);
+
+/* Paged GQA decode: one query row per request.  Enqueues the split kernel,
+ * which writes partials into `workspace`, then the combine kernel, which
+ * writes o (and lse).  workspace_bytes must be >= the plan's workspace_bytes.
+ * Returns astr_status. */
+int astr_paged_decode(const astr_paged_args* a, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Ragged paged prefill with causal offset seq_len - q_len per request.
+ * Needs no workspace (NULL / 0 allowed).  Returns astr_status. */
+int astr_paged_prefill(const astr_paged_args* a, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* astr_last_error(void);
+
+/* ASTR_ABI_VERSION of the built library. */
+int astr_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ASTR_ATTN_H */

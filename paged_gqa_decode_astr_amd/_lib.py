@@ -1,0 +1,210 @@
+"""ctypes binding of libastr_attn.so (argument marshalling only).
+
+The functions here carry the C names (astr_paged_decode, astr_paged_prefill,
+astr_workspace_size, astr_plan_decode, astr_last_error).  They take torch
+tensors, check dtype/device/layout, fill the C argument struct with raw
+pointers, element strides and the current HIP stream, and call the library.
+Every step of the attention runs in the library's HIP kernels; there is no
+other implementation behind these calls.  A missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libastr_attn.so")
+
+ASTR_OK = 0
+ASTR_ERR_INVALID_ARG = 1
+ASTR_ERR_UNSUPPORTED = 2
+ASTR_ERR_WORKSPACE = 3
+ASTR_ERR_HIP = 4
+DEFAULT_MAX_SPLITS = 256
+
+EXPORTED = ("astr_workspace_size", "astr_plan_decode", "astr_paged_decode", "astr_paged_prefill",
+            "astr_last_error", "astr_abi_version")
+
+
+class AstrError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"astr status {status}: {message}")
+        self.status = status
+        self.message = message
+
+
+class PagedArgs(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("num_qo_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("sm_scale", ctypes.c_float),
+        ("q", ctypes.c_void_p), ("q_stride_tok", ctypes.c_int64), ("q_stride_head", ctypes.c_int64),
+        ("o", ctypes.c_void_p), ("o_stride_tok", ctypes.c_int64), ("o_stride_head", ctypes.c_int64),
+        ("lse", ctypes.c_void_p), ("lse_stride_tok", ctypes.c_int64),
+        ("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
+        ("kv_stride_slot", ctypes.c_int64), ("kv_stride_head", ctypes.c_int64), ("num_slots", ctypes.c_int64),
+        ("req_to_token", ctypes.c_void_p), ("req_to_token_stride", ctypes.c_int64),
+        ("kv_indptr", ctypes.c_void_p), ("kv_indptr_host", ctypes.c_void_p),
+        ("qo_indptr", ctypes.c_void_p), ("qo_indptr_host", ctypes.c_void_p),
+        ("num_splits", ctypes.c_int32), ("max_q_len", ctypes.c_int32),
+        ("timing_events", ctypes.c_void_p),
+    ]
+
+
+class DecodePlan(ctypes.Structure):
+    _fields_ = [("num_splits", ctypes.c_int32), ("num_partials", ctypes.c_int32), ("grid_x", ctypes.c_int32),
+                ("grid_y", ctypes.c_int32), ("grid_z", ctypes.c_int32), ("workspace_bytes", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load the built library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m paged_gqa_decode_astr_amd.build` "
+                           "(there is no fallback implementation)")
+    lib = ctypes.CDLL(path)
+    lib.astr_workspace_size.restype = ctypes.c_size_t
+    lib.astr_workspace_size.argtypes = [ctypes.c_int32] * 4
+    lib.astr_plan_decode.restype = ctypes.c_int
+    lib.astr_plan_decode.argtypes = [ctypes.POINTER(PagedArgs), ctypes.c_int32, ctypes.POINTER(DecodePlan)]
+    for fn in ("astr_paged_decode", "astr_paged_prefill"):
+        f = getattr(lib, fn)
+        f.restype = ctypes.c_int
+        f.argtypes = [ctypes.POINTER(PagedArgs), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.astr_last_error.restype = ctypes.c_char_p
+    lib.astr_last_error.argtypes = []
+    lib.astr_abi_version.restype = ctypes.c_int
+    lib.astr_abi_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def astr_last_error() -> str:
+    return load_library().astr_last_error().decode()
+
+
+def astr_workspace_size(batch: int, num_qo_heads: int, head_dim: int, max_splits: int = 0) -> int:
+    return int(load_library().astr_workspace_size(batch, num_qo_heads, head_dim, max_splits))
+
+
+def _check(status: int):
+    if status != ASTR_OK:
+        raise AstrError(status, astr_last_error())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _host_i32(x):
+    """Host int32 copy of an index array (numpy or CPU tensor); kept alive by the caller."""
+    if x is None:
+        return None
+    if hasattr(x, "detach"):
+        x = x.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+def _np_ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def make_args(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host, o, *, sm_scale,
+              req_to_token_stride, lse=None, qo_indptr=None, qo_indptr_host=None, num_splits=0,
+              max_q_len=0, timing_events=None):
+    """Fill the C argument struct from tensors.  Returns (args, keepalive)."""
+    import torch
+
+    for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool), ("o", o)):
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16 (got {t.dtype})")
+        if t.dim() != 3 or t.stride(2) != 1:
+            raise ValueError(f"{name} must be 3-D with a contiguous last dimension")
+    for name, t in (("req_to_token", req_to_token), ("kv_indptr", kv_indptr), ("qo_indptr", qo_indptr)):
+        if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
+            raise TypeError(f"{name} must be a contiguous int32 tensor")
+    if lse is not None and (lse.dtype != torch.float32 or lse.dim() != 2 or lse.stride(1) != 1):
+        raise TypeError("lse must be a 2-D float32 tensor with contiguous last dimension")
+    kvh = _host_i32(kv_indptr_host)
+    qoh = _host_i32(qo_indptr_host)
+    a = PagedArgs()
+    a.batch = kv_indptr.numel() - 1
+    a.num_qo_heads = q.shape[1]
+    a.num_kv_heads = k_pool.shape[1]
+    a.head_dim = q.shape[2]
+    a.sm_scale = float(sm_scale)
+    a.q = _ptr(q)
+    a.q_stride_tok, a.q_stride_head = q.stride(0), q.stride(1)
+    a.o = _ptr(o)
+    a.o_stride_tok, a.o_stride_head = o.stride(0), o.stride(1)
+    a.lse = _ptr(lse)
+    a.lse_stride_tok = lse.stride(0) if lse is not None else 0
+    a.k_pool = _ptr(k_pool)
+    a.v_pool = _ptr(v_pool)
+    if k_pool.stride() != v_pool.stride() or k_pool.shape != v_pool.shape:
+        raise ValueError("k_pool and v_pool must have the same shape and strides")
+    a.kv_stride_slot, a.kv_stride_head = k_pool.stride(0), k_pool.stride(1)
+    a.num_slots = k_pool.shape[0]
+    a.req_to_token = _ptr(req_to_token)
+    a.req_to_token_stride = int(req_to_token_stride)
+    a.kv_indptr = _ptr(kv_indptr)
+    a.kv_indptr_host = _np_ptr(kvh)
+    a.qo_indptr = _ptr(qo_indptr)
+    a.qo_indptr_host = _np_ptr(qoh)
+    a.num_splits = int(num_splits)
+    a.max_q_len = int(max_q_len)
+    ev = None
+    if timing_events is not None:
+        ev = (ctypes.c_void_p * 3)(*[None if e is None else e.cuda_event for e in timing_events])
+        a.timing_events = ctypes.cast(ev, ctypes.c_void_p)
+    return a, (kvh, qoh, ev)
+
+
+def _stream_handle(stream):
+    import torch
+
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def astr_plan_decode(args: PagedArgs, num_cus: int = 0) -> DecodePlan:
+    plan = DecodePlan()
+    _check(load_library().astr_plan_decode(ctypes.byref(args), int(num_cus), ctypes.byref(plan)))
+    return plan
+
+
+def astr_paged_decode(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host, o, workspace, *,
+                      sm_scale, req_to_token_stride, lse=None, num_splits=0, stream=None, timing_events=None):
+    """Paged GQA decode: q [B, Hq, D] bf16 -> o [B, Hq, D] bf16 (+ lse [B, Hq] fp32).
+
+    timing_events: optional 3 torch.cuda.Event(enable_timing=True) recorded
+    before the split kernel, between split and combine, and after combine."""
+    lib = load_library()
+    a, keep = make_args(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host, o, sm_scale=sm_scale,
+                        req_to_token_stride=req_to_token_stride, lse=lse, num_splits=num_splits,
+                        timing_events=timing_events)
+    ws_ptr = _ptr(workspace)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.astr_paged_decode(ctypes.byref(a), ws_ptr, ws_bytes, _stream_handle(stream)))
+    del keep
+
+
+def astr_paged_prefill(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host, qo_indptr, qo_indptr_host,
+                       o, *, sm_scale, req_to_token_stride, lse=None, max_q_len=0, stream=None,
+                       timing_events=None):
+    """Ragged paged prefill: q [sum q_len, Hq, D] bf16 in qo_indptr order -> o (+ lse).
+
+    timing_events: optional 2 torch.cuda.Event(enable_timing=True) recorded
+    before and after the kernel."""
+    lib = load_library()
+    a, keep = make_args(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host, o, sm_scale=sm_scale,
+                        req_to_token_stride=req_to_token_stride, lse=lse, qo_indptr=qo_indptr,
+                        qo_indptr_host=qo_indptr_host, max_q_len=max_q_len, timing_events=timing_events)
+    _check(lib.astr_paged_prefill(ctypes.byref(a), None, 0, _stream_handle(stream)))
+    del keep

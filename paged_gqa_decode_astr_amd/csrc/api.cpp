@@ -1,0 +1,317 @@
+// C ABI of the paged GQA attention library: argument validation, the split
+// planner, workspace layout and kernel launches.  See include/astr_attn.h for
+// the contract of each entry point.
+//
+// Validation mirrors the reference backend's habit of checking a forward call
+// before touching the KV cache ([attention.py @c9ceca1], the commit that adds a
+// shared forward guard and validates prefill inputs before KV allocation): all
+// checks run on the host, before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "astr_attn.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return ASTR_OK;
+}
+
+// Planner constants (work groups per CU, fewest keys per work group, cap).
+constexpr int64_t kWgPerCu = 2;
+constexpr int64_t kMinTokens = 64;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+int64_t partial_bytes(int64_t batch, int64_t hq, int64_t d, int64_t splits) {
+  const int64_t P = splits + batch - 1;
+  return align256(hq * P * d * 4) + hq * P * 2 * 4;
+}
+
+// Per-device compute-unit count, cached after the first query.
+std::mutex g_cu_mu;
+std::vector<int> g_cu_count;
+
+int device_cu_count(int* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(ASTR_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lk(g_cu_mu);
+  if ((int)g_cu_count.size() <= dev) g_cu_count.resize(dev + 1, 0);
+  if (g_cu_count[dev] == 0) {
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return fail(ASTR_ERR_HIP, "hipDeviceGetAttribute: %s", hipGetErrorString(e));
+    g_cu_count[dev] = n;
+  }
+  *out = g_cu_count[dev];
+  return ASTR_OK;
+}
+
+// Checks shared by decode and prefill.  Sets *total_keys = kv_indptr[B].
+int validate_common(const astr_paged_args* a, bool prefill, int64_t* total_keys) {
+  if (a == nullptr) return fail(ASTR_ERR_INVALID_ARG, "args is NULL");
+  if (a->batch < 0) return fail(ASTR_ERR_INVALID_ARG, "batch must be >= 0 (got %d)", a->batch);
+  if (a->num_qo_heads < 1 || a->num_kv_heads < 1)
+    return fail(ASTR_ERR_INVALID_ARG, "head counts must be >= 1 (Hq=%d, Hkv=%d)", a->num_qo_heads, a->num_kv_heads);
+  if (a->batch > 65535 || a->num_kv_heads > 65535)
+    return fail(ASTR_ERR_INVALID_ARG, "batch (%d) and num_kv_heads (%d) must be <= 65535 (grid limits)", a->batch,
+                a->num_kv_heads);
+  if (a->num_qo_heads % a->num_kv_heads != 0)
+    return fail(ASTR_ERR_INVALID_ARG, "num_qo_heads (%d) must be a multiple of num_kv_heads (%d)", a->num_qo_heads,
+                a->num_kv_heads);
+  const int group = a->num_qo_heads / a->num_kv_heads;
+  const bool supported = prefill ? astr::prefill_supported(a->head_dim, group) : astr::decode_supported(a->head_dim, group);
+  if (!supported)
+    return fail(ASTR_ERR_UNSUPPORTED, "no kernel for head_dim=%d and group size %d (head_dim in {64,128}, group in {1,2,4,8})",
+                a->head_dim, group);
+  if (!(a->sm_scale == a->sm_scale) || a->sm_scale == __builtin_inff() || a->sm_scale == -__builtin_inff())
+    return fail(ASTR_ERR_INVALID_ARG, "sm_scale must be finite");
+  *total_keys = 0;
+  if (a->batch == 0) return ASTR_OK;
+
+  struct { const void* p; const char* name; } req[] = {
+      {a->q, "q"}, {a->o, "o"}, {a->k_pool, "k_pool"}, {a->v_pool, "v_pool"},
+      {a->req_to_token, "req_to_token"}, {a->kv_indptr, "kv_indptr"}, {a->kv_indptr_host, "kv_indptr_host"}};
+  for (auto& r : req)
+    if (r.p == nullptr) return fail(ASTR_ERR_INVALID_ARG, "%s is NULL", r.name);
+  if (!aligned16(a->q) || !aligned16(a->o) || !aligned16(a->k_pool) || !aligned16(a->v_pool))
+    return fail(ASTR_ERR_INVALID_ARG, "q, o, k_pool and v_pool must be 16-byte aligned");
+  struct { int64_t v; const char* name; } strides[] = {
+      {a->q_stride_tok, "q_stride_tok"}, {a->q_stride_head, "q_stride_head"}, {a->o_stride_tok, "o_stride_tok"},
+      {a->o_stride_head, "o_stride_head"}, {a->kv_stride_slot, "kv_stride_slot"}, {a->kv_stride_head, "kv_stride_head"}};
+  for (auto& s : strides)
+    if (s.v <= 0 || s.v % 8 != 0)
+      return fail(ASTR_ERR_INVALID_ARG, "%s must be a positive multiple of 8 elements (got %lld)", s.name, (long long)s.v);
+  if (a->lse != nullptr) {
+    if ((reinterpret_cast<uintptr_t>(a->lse) & 3u) != 0) return fail(ASTR_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+    if (a->lse_stride_tok < 1) return fail(ASTR_ERR_INVALID_ARG, "lse_stride_tok must be >= 1");
+  }
+  if (a->num_slots < 1 || a->num_slots > (int64_t)INT32_MAX + 1)
+    return fail(ASTR_ERR_INVALID_ARG, "num_slots must be in [1, 2^31] (got %lld)", (long long)a->num_slots);
+  if (a->req_to_token_stride < 0) return fail(ASTR_ERR_INVALID_ARG, "req_to_token_stride must be >= 0");
+
+  const int32_t* kv = a->kv_indptr_host;
+  if (kv[0] != 0) return fail(ASTR_ERR_INVALID_ARG, "kv_indptr[0] must be 0 (got %d)", kv[0]);
+  for (int b = 0; b < a->batch; ++b) {
+    const int64_t L = (int64_t)kv[b + 1] - kv[b];
+    if (L < 1) return fail(ASTR_ERR_INVALID_ARG, "request %d: seq_len must be >= 1 (got %lld)", b, (long long)L);
+    if (a->req_to_token_stride > 0 && L > a->req_to_token_stride)
+      return fail(ASTR_ERR_INVALID_ARG, "request %d: seq_len %lld exceeds req_to_token_stride %lld", b, (long long)L,
+                  (long long)a->req_to_token_stride);
+  }
+  *total_keys = kv[a->batch];
+  return ASTR_OK;
+}
+
+// Records timing_events[i] on the stream when the caller asked for it.
+int record_event(void* const* events, int i, hipStream_t s) {
+  if (events == nullptr || events[i] == nullptr) return ASTR_OK;
+  hipError_t e = hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
+  if (e != hipSuccess) return fail(ASTR_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+  return ASTR_OK;
+}
+
+int plan_decode_impl(const astr_paged_args* a, int64_t total_keys, int32_t num_cus, astr_decode_plan* out) {
+  int64_t wh;
+  if (a->num_splits > 0) {
+    wh = a->num_splits;
+  } else if (a->num_splits < 0) {
+    return fail(ASTR_ERR_INVALID_ARG, "num_splits must be >= 0 (got %d)", a->num_splits);
+  } else {
+    const int64_t target = ceil_div(kWgPerCu * (int64_t)num_cus, a->num_kv_heads);
+    const int64_t by_len = total_keys > 0 ? ceil_div(total_keys, kMinTokens) : 1;
+    wh = target < by_len ? target : by_len;
+    if (wh > ASTR_DEFAULT_MAX_SPLITS) wh = ASTR_DEFAULT_MAX_SPLITS;
+    if (wh < 1) wh = 1;
+  }
+  if (wh > 65535) return fail(ASTR_ERR_INVALID_ARG, "num_splits %lld exceeds 65535", (long long)wh);
+  out->num_splits = (int32_t)wh;
+  out->num_partials = (int32_t)(wh + a->batch - 1);
+  out->grid_x = (int32_t)wh;
+  out->grid_y = a->num_kv_heads;
+  out->grid_z = 1;
+  out->workspace_bytes = a->batch > 0 ? partial_bytes(a->batch, a->num_qo_heads, a->head_dim, wh) : 0;
+  return ASTR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* astr_last_error(void) { return g_err; }
+
+int astr_abi_version(void) { return ASTR_ABI_VERSION; }
+
+size_t astr_workspace_size(int32_t batch, int32_t num_qo_heads, int32_t head_dim, int32_t max_splits) {
+  if (batch < 1 || num_qo_heads < 1 || head_dim < 1 || max_splits < 0) return 0;
+  const int64_t cap = max_splits == 0 ? ASTR_DEFAULT_MAX_SPLITS : max_splits;
+  return (size_t)partial_bytes(batch, num_qo_heads, head_dim, cap);
+}
+
+int astr_plan_decode(const astr_paged_args* a, int32_t num_cus, astr_decode_plan* out) {
+  if (out == nullptr) return fail(ASTR_ERR_INVALID_ARG, "plan output is NULL");
+  if (a == nullptr) return fail(ASTR_ERR_INVALID_ARG, "args is NULL");
+  int64_t total = 0;
+  if (a->num_splits == 0) {
+    // The automatic plan needs the host copy of kv_indptr.
+    if (a->batch < 0) return fail(ASTR_ERR_INVALID_ARG, "batch must be >= 0 (got %d)", a->batch);
+    if (a->batch > 0 && a->kv_indptr_host == nullptr) return fail(ASTR_ERR_INVALID_ARG, "kv_indptr_host is NULL");
+    if (a->batch > 0) total = a->kv_indptr_host[a->batch] - a->kv_indptr_host[0];
+  }
+  if (num_cus <= 0) {
+    int st = device_cu_count(&num_cus);
+    if (st != ASTR_OK) return st;
+  }
+  if (a->num_kv_heads < 1) return fail(ASTR_ERR_INVALID_ARG, "num_kv_heads must be >= 1");
+  const int st = plan_decode_impl(a, total, num_cus, out);
+  return st == ASTR_OK ? ok() : st;
+}
+
+int astr_paged_decode(const astr_paged_args* a, void* workspace, size_t workspace_bytes, void* stream) {
+  int64_t total = 0;
+  int st = validate_common(a, false, &total);
+  if (st != ASTR_OK) return st;
+  if (a->qo_indptr != nullptr || a->qo_indptr_host != nullptr)
+    return fail(ASTR_ERR_INVALID_ARG, "decode takes no qo_indptr (one query row per request)");
+  if (a->batch == 0) return ok();
+  int num_cus = 0;
+  if (a->num_splits == 0) {
+    st = device_cu_count(&num_cus);
+    if (st != ASTR_OK) return st;
+  }
+  astr_decode_plan plan;
+  st = plan_decode_impl(a, total, num_cus, &plan);
+  if (st != ASTR_OK) return st;
+  if (workspace == nullptr) return fail(ASTR_ERR_WORKSPACE, "decode needs a workspace of %lld bytes", (long long)plan.workspace_bytes);
+  if (!aligned16(workspace)) return fail(ASTR_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  if ((int64_t)workspace_bytes < plan.workspace_bytes)
+    return fail(ASTR_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %lld bytes the plan needs", workspace_bytes,
+                (long long)plan.workspace_bytes);
+
+  astr::DecodeLaunch p;
+  p.batch = a->batch;
+  p.num_qo_heads = a->num_qo_heads;
+  p.num_kv_heads = a->num_kv_heads;
+  p.head_dim = a->head_dim;
+  p.group = a->num_qo_heads / a->num_kv_heads;
+  p.sm_scale = a->sm_scale;
+  p.q = static_cast<const uint16_t*>(a->q);
+  p.q_stride_tok = a->q_stride_tok;
+  p.q_stride_head = a->q_stride_head;
+  p.o = static_cast<uint16_t*>(a->o);
+  p.o_stride_tok = a->o_stride_tok;
+  p.o_stride_head = a->o_stride_head;
+  p.lse = a->lse;
+  p.lse_stride_tok = a->lse_stride_tok;
+  p.k_pool = static_cast<const uint16_t*>(a->k_pool);
+  p.v_pool = static_cast<const uint16_t*>(a->v_pool);
+  p.kv_stride_slot = a->kv_stride_slot;
+  p.kv_stride_head = a->kv_stride_head;
+  p.req_to_token = a->req_to_token;
+  p.req_to_token_stride = a->req_to_token_stride;
+  p.kv_indptr = a->kv_indptr;
+  p.num_splits = plan.num_splits;
+  p.num_partials = plan.num_partials;
+  p.o_part = static_cast<float*>(workspace);
+  p.ml_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                       align256((int64_t)a->num_qo_heads * plan.num_partials * a->head_dim * 4));
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int st2 = record_event(a->timing_events, 0, s);
+  if (st2 != ASTR_OK) return st2;
+  hipError_t e = astr::launch_decode_split(p, s);
+  if (e != hipSuccess) return fail(ASTR_ERR_HIP, "split kernel launch: %s", hipGetErrorString(e));
+  st2 = record_event(a->timing_events, 1, s);
+  if (st2 != ASTR_OK) return st2;
+  e = astr::launch_decode_combine(p, s);
+  if (e != hipSuccess) return fail(ASTR_ERR_HIP, "combine kernel launch: %s", hipGetErrorString(e));
+  st2 = record_event(a->timing_events, 2, s);
+  if (st2 != ASTR_OK) return st2;
+  return ok();
+}
+
+int astr_paged_prefill(const astr_paged_args* a, void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  int64_t total = 0;
+  int st = validate_common(a, true, &total);
+  if (st != ASTR_OK) return st;
+  if (a->batch == 0) return ok();
+  if (a->qo_indptr == nullptr || a->qo_indptr_host == nullptr)
+    return fail(ASTR_ERR_INVALID_ARG, "prefill needs qo_indptr and qo_indptr_host");
+  if (a->max_q_len < 0) return fail(ASTR_ERR_INVALID_ARG, "max_q_len must be >= 0");
+  const int32_t* qo = a->qo_indptr_host;
+  const int32_t* kv = a->kv_indptr_host;
+  if (qo[0] != 0) return fail(ASTR_ERR_INVALID_ARG, "qo_indptr[0] must be 0 (got %d)", qo[0]);
+  int32_t max_q = 0;
+  for (int b = 0; b < a->batch; ++b) {
+    const int64_t ql = (int64_t)qo[b + 1] - qo[b];
+    const int64_t L = (int64_t)kv[b + 1] - kv[b];
+    if (ql < 1 || ql > L)
+      return fail(ASTR_ERR_INVALID_ARG, "request %d: need 1 <= q_len <= seq_len (q_len %lld, seq_len %lld)", b, (long long)ql,
+                  (long long)L);
+    if (ql > max_q) max_q = (int32_t)ql;
+  }
+  if (a->max_q_len > 0) {
+    if (max_q > a->max_q_len)
+      return fail(ASTR_ERR_INVALID_ARG, "a q_len of %d exceeds max_q_len %d", max_q, a->max_q_len);
+    max_q = a->max_q_len;
+  }
+
+  astr::PrefillLaunch p;
+  p.batch = a->batch;
+  p.num_qo_heads = a->num_qo_heads;
+  p.num_kv_heads = a->num_kv_heads;
+  p.head_dim = a->head_dim;
+  p.group = a->num_qo_heads / a->num_kv_heads;
+  p.sm_scale = a->sm_scale;
+  p.q = static_cast<const uint16_t*>(a->q);
+  p.q_stride_tok = a->q_stride_tok;
+  p.q_stride_head = a->q_stride_head;
+  p.o = static_cast<uint16_t*>(a->o);
+  p.o_stride_tok = a->o_stride_tok;
+  p.o_stride_head = a->o_stride_head;
+  p.lse = a->lse;
+  p.lse_stride_tok = a->lse_stride_tok;
+  p.k_pool = static_cast<const uint16_t*>(a->k_pool);
+  p.v_pool = static_cast<const uint16_t*>(a->v_pool);
+  p.kv_stride_slot = a->kv_stride_slot;
+  p.kv_stride_head = a->kv_stride_head;
+  p.req_to_token = a->req_to_token;
+  p.req_to_token_stride = a->req_to_token_stride;
+  p.kv_indptr = a->kv_indptr;
+  p.qo_indptr = a->qo_indptr;
+  p.max_q_len = max_q;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = record_event(a->timing_events, 0, s);
+  if (st != ASTR_OK) return st;
+  hipError_t e = astr::launch_prefill(p, s);
+  if (e != hipSuccess) return fail(ASTR_ERR_HIP, "prefill kernel launch: %s", hipGetErrorString(e));
+  st = record_event(a->timing_events, 1, s);
+  if (st != ASTR_OK) return st;
+  return ok();
+}
+
+}  // extern "C"

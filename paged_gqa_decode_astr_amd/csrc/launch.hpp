@@ -1,0 +1,59 @@
+// Host-side launch descriptors shared by the C ABI layer and the HIP kernels.
+// Plain structs: every field is already validated by the ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace astr {
+
+struct DecodeLaunch {
+  int32_t batch, num_qo_heads, num_kv_heads, head_dim, group;
+  float sm_scale;
+  const uint16_t* q;
+  int64_t q_stride_tok, q_stride_head;
+  uint16_t* o;
+  int64_t o_stride_tok, o_stride_head;
+  float* lse;
+  int64_t lse_stride_tok;
+  const uint16_t* k_pool;
+  const uint16_t* v_pool;
+  int64_t kv_stride_slot, kv_stride_head;
+  const int32_t* req_to_token;
+  int64_t req_to_token_stride;
+  const int32_t* kv_indptr;
+  int32_t num_splits;    // Wh: work groups per kv head (grid.x)
+  int32_t num_partials;  // P = Wh + B - 1 slots per query head
+  float* o_part;         // [Hq][P][D]
+  float* ml_part;        // [Hq][P][2]
+};
+
+struct PrefillLaunch {
+  int32_t batch, num_qo_heads, num_kv_heads, head_dim, group;
+  float sm_scale;
+  const uint16_t* q;
+  int64_t q_stride_tok, q_stride_head;
+  uint16_t* o;
+  int64_t o_stride_tok, o_stride_head;
+  float* lse;
+  int64_t lse_stride_tok;
+  const uint16_t* k_pool;
+  const uint16_t* v_pool;
+  int64_t kv_stride_slot, kv_stride_head;
+  const int32_t* req_to_token;
+  int64_t req_to_token_stride;
+  const int32_t* kv_indptr;
+  const int32_t* qo_indptr;
+  int32_t max_q_len;     // grid covers query positions [0, max_q_len)
+};
+
+// Each returns the launch status (hipGetLastError after the launch).
+hipError_t launch_decode_split(const DecodeLaunch& p, hipStream_t stream);
+hipError_t launch_decode_combine(const DecodeLaunch& p, hipStream_t stream);
+hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream);
+
+// Whether a (head_dim, group) pair has a compiled kernel.
+bool decode_supported(int head_dim, int group);
+bool prefill_supported(int head_dim, int group);
+
+}  // namespace astr

@@ -1,0 +1,69 @@
+"""Move seeded inputs (numpy bit patterns from workloads.py) onto the GPU and
+allocate outputs / workspaces with torch.  Memory plumbing only."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import _lib
+
+
+def bf16_tensor(bits: np.ndarray, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+def to_device(inp: dict, device="cuda") -> dict:
+    """Device copies of one batch from workloads.build_paged_inputs / make_inputs."""
+    d = {
+        "q": bf16_tensor(inp["q"], device),
+        "k_pool": bf16_tensor(inp["k_pool"], device),
+        "v_pool": bf16_tensor(inp["v_pool"], device),
+        "req_to_token": torch.from_numpy(np.ascontiguousarray(inp["req_to_token"])).to(device),
+        "kv_indptr": torch.from_numpy(inp["kv_indptr"]).to(device),
+        "kv_indptr_host": np.ascontiguousarray(inp["kv_indptr"], dtype=np.int32),
+        "req_to_token_stride": int(inp["req_to_token_stride"]),
+        "sm_scale": float(inp["sm_scale"]),
+        "qo_indptr": None, "qo_indptr_host": None,
+    }
+    if inp.get("qo_indptr") is not None:
+        d["qo_indptr"] = torch.from_numpy(inp["qo_indptr"]).to(device)
+        d["qo_indptr_host"] = np.ascontiguousarray(inp["qo_indptr"], dtype=np.int32)
+    return d
+
+
+def decode_workspace(batch: int, num_qo_heads: int, head_dim: int, device="cuda", max_splits: int = 0,
+                     fill: float | None = None) -> torch.Tensor:
+    nbytes = _lib.astr_workspace_size(batch, num_qo_heads, head_dim, max_splits)
+    n = (nbytes + 3) // 4
+    if fill is None:
+        return torch.empty(n, dtype=torch.float32, device=device)
+    return torch.full((n,), fill, dtype=torch.float32, device=device)
+
+
+def run_decode(dev: dict, o=None, lse=None, workspace=None, num_splits=0, stream=None, timing_events=None):
+    q = dev["q"]
+    if o is None:
+        o = torch.empty_like(q)
+    if workspace is None:
+        workspace = decode_workspace(q.shape[0], q.shape[1], q.shape[2], q.device,
+                                     max_splits=max(num_splits, 0))
+    _lib.astr_paged_decode(q, dev["k_pool"], dev["v_pool"], dev["req_to_token"], dev["kv_indptr"],
+                           dev["kv_indptr_host"], o, workspace, sm_scale=dev["sm_scale"],
+                           req_to_token_stride=dev["req_to_token_stride"], lse=lse, num_splits=num_splits,
+                           stream=stream, timing_events=timing_events)
+    return o
+
+
+def run_prefill(dev: dict, o=None, lse=None, max_q_len=0, stream=None, timing_events=None):
+    q = dev["q"]
+    if o is None:
+        o = torch.empty_like(q)
+    _lib.astr_paged_prefill(q, dev["k_pool"], dev["v_pool"], dev["req_to_token"], dev["kv_indptr"],
+                            dev["kv_indptr_host"], dev["qo_indptr"], dev["qo_indptr_host"], o,
+                            sm_scale=dev["sm_scale"], req_to_token_stride=dev["req_to_token_stride"], lse=lse,
+                            max_q_len=max_q_len, stream=stream, timing_events=timing_events)
+    return o
+
+
+def bf16_to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to(torch.float64).cpu().numpy()

@@ -1,0 +1,41 @@
+"""Shared helpers for the GPU parity tests (oracle on the host, HIP path on the GPU)."""
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from paged_gqa_decode_astr_amd import tensors
+
+ATOL = 1e-2   # max-abs bar against the fp64 oracle
+RTOL = 2e-2   # max-rel bar against the fp64 oracle
+
+
+def announce(msg: str):
+    """Name the case before a GPU step, flushed, so a dying run still says what it ran."""
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def oracle_of(inp):
+    return oracle.paged_attention(inp["q"], inp["k_pool"], inp["v_pool"], inp["req_to_token"],
+                                  inp["req_to_token_stride"], inp["kv_indptr"], inp["sm_scale"],
+                                  qo_indptr=inp.get("qo_indptr"))
+
+
+def assert_close(got: torch.Tensor, ref: np.ndarray, what: str, atol=ATOL, rtol=RTOL):
+    """Element-wise |got - ref| <= atol + rtol |ref|, plus max-abs <= atol on its own."""
+    g = tensors.bf16_to_f64(got) if got.dtype == torch.bfloat16 else got.detach().double().cpu().numpy()
+    assert g.shape == ref.shape, (g.shape, ref.shape)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    err = np.abs(g - ref)
+    bad = err > atol + rtol * np.abs(ref)
+    big = np.abs(ref) >= 1e-2
+    max_rel = float((err[big] / np.abs(ref[big])).max()) if big.any() else 0.0
+    msg = f"{what}: max_abs={err.max():.3e} max_rel(|ref|>=1e-2)={max_rel:.3e} bad={int(bad.sum())}"
+    if bad.any():
+        idx = np.unravel_index(np.argmax(err - (atol + rtol * np.abs(ref))), err.shape)
+        msg += f" worst at {idx}: got {g[idx]} ref {ref[idx]}"
+    assert not bad.any(), msg
+    assert err.max() <= atol, msg
+    return float(err.max()), max_rel

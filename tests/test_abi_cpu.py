@@ -1,0 +1,185 @@
+"""Host-side checks of the C-ABI library: exports, workspace sizing, the split
+planner against the oracle's independent statement of it, and argument
+validation.  No call here reaches a kernel launch (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from paged_gqa_decode_astr_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    header = open(os.path.join(ROOT, "include", "astr_attn.h")).read()
+    declared = set(re.findall(r"^\s*(?:size_t|int|const char\*)\s+(astr_\w+)\s*\(", header, re.M))
+    assert declared == set(_lib.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert lib.astr_abi_version() == 1
+
+
+def test_workspace_size_formula(lib):
+    for B, Hq, D, S in [(32, 32, 128, 0), (1, 4, 64, 7), (256, 32, 128, 64)]:
+        cap = 256 if S == 0 else S
+        P = cap + B - 1
+        want = ((Hq * P * D * 4 + 255) // 256) * 256 + Hq * P * 8
+        assert _lib.astr_workspace_size(B, Hq, D, S) == want
+    assert _lib.astr_workspace_size(0, 32, 128, 0) == 0
+    assert _lib.astr_workspace_size(4, 32, 128, -1) == 0
+
+
+def _args(kv_indptr, Hq=32, Hkv=8, D=128, num_splits=0):
+    a = _lib.PagedArgs()
+    a.batch = len(kv_indptr) - 1
+    a.num_qo_heads, a.num_kv_heads, a.head_dim = Hq, Hkv, D
+    kvh = np.ascontiguousarray(kv_indptr, dtype=np.int32)
+    a.kv_indptr_host = kvh.ctypes.data_as(ctypes.c_void_p)
+    a.num_splits = num_splits
+    return a, kvh
+
+
+def test_plan_matches_oracle_random():
+    rng = np.random.default_rng(2024)
+    for _ in range(3000):
+        B = int(rng.integers(1, 300))
+        hi = int(rng.choice([8, 64, 2000, 40000]))
+        L = rng.integers(1, hi + 1, size=B)
+        kv = np.concatenate([[0], np.cumsum(L)])
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        cus = int(rng.choice([1, 80, 256, 304]))
+        a, keep = _args(kv, Hq=Hkv * 4, Hkv=Hkv)
+        plan = _lib.astr_plan_decode(a, cus)
+        want = oracle.plan_num_splits(kv, Hkv, cus)
+        assert plan.num_splits == want
+        assert plan.num_partials == want + B - 1
+        assert (plan.grid_x, plan.grid_y, plan.grid_z) == (want, Hkv, 1)
+        assert plan.workspace_bytes == _lib.astr_workspace_size(B, Hkv * 4, 128, want)
+
+
+def test_plan_config_examples():
+    from paged_gqa_decode_astr_amd.workloads import make_inputs
+    for cid, want in [("tiny", None), ("decode_b32", 64)]:
+        inp = make_inputs(cid, 0)
+        a, keep = _args(inp["kv_indptr"], inp["num_qo_heads"], inp["num_kv_heads"], inp["head_dim"])
+        plan = _lib.astr_plan_decode(a, 256)
+        assert plan.num_splits == oracle.plan_num_splits(inp["kv_indptr"], inp["num_kv_heads"], 256)
+        if want is not None:
+            assert plan.num_splits == want
+
+
+def test_plan_forced_and_errors():
+    a, keep = _args([0, 5, 9], num_splits=3)
+    assert _lib.astr_plan_decode(a, 256).num_splits == 3
+    a.num_splits = -1
+    with pytest.raises(_lib.AstrError) as ei:
+        _lib.astr_plan_decode(a, 256)
+    assert ei.value.status == _lib.ASTR_ERR_INVALID_ARG
+
+
+# --------------------------------------------------------------------------- validation
+
+FAKE = 0x10000  # 16-byte aligned stand-in for device pointers; never dereferenced on the host
+
+
+def _valid_decode_args(kv=(0, 3, 7)):
+    a, kvh = _args(list(kv), Hq=8, Hkv=2, D=64)
+    a.sm_scale = 0.125
+    for f in ("q", "o", "k_pool", "v_pool", "req_to_token", "kv_indptr"):
+        setattr(a, f, FAKE)
+    a.q_stride_tok, a.q_stride_head = 8 * 64, 64
+    a.o_stride_tok, a.o_stride_head = 8 * 64, 64
+    a.kv_stride_slot, a.kv_stride_head = 2 * 64, 64
+    a.num_slots = 64
+    a.req_to_token_stride = 8
+    return a, kvh
+
+
+def _call_decode(a, ws=FAKE, nbytes=1 << 30):
+    lib = _lib.load_library()
+    return lib.astr_paged_decode(ctypes.byref(a), ws, nbytes, None)
+
+
+def _call_prefill(a):
+    lib = _lib.load_library()
+    return lib.astr_paged_prefill(ctypes.byref(a), None, 0, None)
+
+
+@pytest.mark.parametrize("mutate,status,needle", [
+    (lambda a: setattr(a, "q", None), 1, "q is NULL"),
+    (lambda a: setattr(a, "kv_indptr_host", None), 1, "kv_indptr_host is NULL"),
+    (lambda a: setattr(a, "num_kv_heads", 3), 1, "multiple"),
+    (lambda a: setattr(a, "head_dim", 96), 2, "head_dim"),
+    (lambda a: (setattr(a, "num_qo_heads", 32), setattr(a, "num_kv_heads", 2)), 2, "group"),
+    (lambda a: setattr(a, "q", FAKE + 8), 1, "aligned"),
+    (lambda a: setattr(a, "kv_stride_head", 60), 1, "kv_stride_head"),
+    (lambda a: setattr(a, "o_stride_tok", 0), 1, "o_stride_tok"),
+    (lambda a: setattr(a, "sm_scale", float("nan")), 1, "sm_scale"),
+    (lambda a: setattr(a, "req_to_token_stride", 3), 1, "exceeds req_to_token_stride"),
+    (lambda a: setattr(a, "num_slots", 0), 1, "num_slots"),
+    (lambda a: setattr(a, "batch", -1), 1, "batch"),
+    (lambda a: setattr(a, "qo_indptr", FAKE), 1, "no qo_indptr"),
+    (lambda a: setattr(a, "num_splits", -2), 1, "num_splits"),
+])
+def test_decode_rejects_bad_arguments(mutate, status, needle):
+    a, keep = _valid_decode_args()
+    mutate(a)
+    assert _call_decode(a) == status
+    assert needle in _lib.astr_last_error()
+
+
+@pytest.mark.parametrize("kv,needle", [((1, 3, 7), "kv_indptr[0]"), ((0, 3, 3), "seq_len must be >= 1"),
+                                       ((0, 5, 2), "seq_len must be >= 1")])
+def test_decode_rejects_bad_indptr(kv, needle):
+    a, keep = _valid_decode_args(kv)
+    assert _call_decode(a) == _lib.ASTR_ERR_INVALID_ARG
+    assert needle in _lib.astr_last_error()
+
+
+def test_decode_workspace_checks():
+    a, keep = _valid_decode_args()
+    a.num_splits = 4
+    assert _call_decode(a, ws=None) == _lib.ASTR_ERR_WORKSPACE
+    need = _lib.astr_workspace_size(2, 8, 64, 4)
+    assert _call_decode(a, nbytes=need - 1) == _lib.ASTR_ERR_WORKSPACE
+    assert "smaller" in _lib.astr_last_error()
+    assert _call_decode(a, ws=FAKE + 4, nbytes=need) == _lib.ASTR_ERR_WORKSPACE
+
+
+def test_empty_batch_is_a_noop():
+    a, keep = _valid_decode_args((0,))
+    assert _call_decode(a, ws=None, nbytes=0) == _lib.ASTR_OK
+    a2, keep2 = _valid_decode_args((0,))
+    assert _call_prefill(a2) == _lib.ASTR_OK
+
+
+def _valid_prefill_args(kv=(0, 3, 7), qo=(0, 2, 3)):
+    a, kvh = _valid_decode_args(kv)
+    qoh = np.ascontiguousarray(qo, dtype=np.int32)
+    a.qo_indptr = FAKE
+    a.qo_indptr_host = qoh.ctypes.data_as(ctypes.c_void_p)
+    return a, (kvh, qoh)
+
+
+@pytest.mark.parametrize("qo,max_q,needle", [((0, 0, 3), 0, "q_len"), ((0, 4, 5), 0, "q_len"),
+                                             ((1, 2, 3), 0, "qo_indptr[0]"), ((0, 2, 3), 1, "max_q_len")])
+def test_prefill_rejects_bad_qlens(qo, max_q, needle):
+    a, keep = _valid_prefill_args(qo=qo)
+    a.max_q_len = max_q
+    assert _call_prefill(a) == _lib.ASTR_ERR_INVALID_ARG
+    assert needle in _lib.astr_last_error()
+
+
+def test_prefill_needs_qo_indptr():
+    a, keep = _valid_decode_args()
+    assert _call_prefill(a) == _lib.ASTR_ERR_INVALID_ARG
+    assert "qo_indptr" in _lib.astr_last_error()
