@@ -119,6 +119,7 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget (0 = skip)")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--probe", action="store_true", help="also measure torch copy / row-gather bandwidth ceilings")
+    ap.add_argument("--num-splits", type=int, default=0, help="decode work groups per kv head (0 = library plan)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -128,6 +129,7 @@ def main(argv=None):
 
     import torch
     from paged_gqa_decode_astr_amd import _lib, tensors
+    from paged_gqa_decode_astr_amd.hip_events import HipEvent
     from paged_gqa_decode_astr_amd.workloads import CONFIGS, make_inputs
 
     _lib.load_library()
@@ -141,13 +143,14 @@ def main(argv=None):
         B, Hq, D = inp["q"].shape
         d["o"] = torch.empty(B, Hq, D, dtype=torch.bfloat16, device=dev)
         d["lse"] = torch.empty(B, Hq, dtype=torch.float32, device=dev)
-        d["ws"] = tensors.decode_workspace(B, Hq, D, dev)
+        d["ws"] = tensors.decode_workspace(B, Hq, D, dev, max_splits=args.num_splits)
         sets.append((inp, d))
     torch.cuda.synchronize()
 
     def step(k, events=None):
         _, d = sets[k % len(sets)]
-        tensors.run_decode(d, o=d["o"], lse=d["lse"], workspace=d["ws"], timing_events=events)
+        tensors.run_decode(d, o=d["o"], lse=d["lse"], workspace=d["ws"], timing_events=events,
+                           num_splits=args.num_splits)
 
     log(f"[bench] warmup {args.warmup}")
     for k in range(args.warmup):
@@ -169,7 +172,7 @@ def main(argv=None):
 
     # Per-kernel durations: events recorded by the library around each kernel, same stream.
     log("[bench] per-kernel event timing")
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[HipEvent() for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for k in range(args.steps):
         step(k, evs[k])
@@ -181,7 +184,7 @@ def main(argv=None):
     plan = _lib.astr_plan_decode(_lib.make_args(
         sets[0][1]["q"], sets[0][1]["k_pool"], sets[0][1]["v_pool"], sets[0][1]["req_to_token"],
         sets[0][1]["kv_indptr"], sets[0][1]["kv_indptr_host"], sets[0][1]["o"], sm_scale=1.0,
-        req_to_token_stride=sets[0][1]["req_to_token_stride"])[0], 0)
+        req_to_token_stride=sets[0][1]["req_to_token_stride"], num_splits=args.num_splits)[0], 0)
 
     B, Hq, D = sets[0][0]["q"].shape
     G = Hq // cfg.num_kv_heads
@@ -214,7 +217,7 @@ def main(argv=None):
             tensors.run_prefill(pd, o=po, lse=plse)
         torch.cuda.synchronize()
         psteps = max(10, args.steps // 4)
-        pev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(psteps)]
+        pev = [[HipEvent() for _ in range(2)] for _ in range(psteps)]
         for k in range(psteps):
             tensors.run_prefill(pd, o=po, lse=plse, timing_events=pev[k] + [None])
         torch.cuda.synchronize()

@@ -23,8 +23,15 @@ def oracle_of(inp):
                                   qo_indptr=inp.get("qo_indptr"))
 
 
-def assert_close(got: torch.Tensor, ref: np.ndarray, what: str, atol=ATOL, rtol=RTOL):
-    """Element-wise |got - ref| <= atol + rtol |ref|, plus max-abs <= atol on its own."""
+def assert_close(got: torch.Tensor, ref: np.ndarray, what: str, atol=ATOL, rtol=RTOL, ulp_check=True):
+    """Element-wise |got - ref| <= atol + rtol |ref| (max-abs 1e-2 and max-rel 2e-2 read together).
+
+    An absolute bound alone cannot hold for a bf16 output: for |O| in [4, 8) the
+    rounding step alone is up to 2^-6 = 0.0156.  Also checked: the output is
+    within one bf16 ulp of the fp64 value plus a small fp32 margin (ulp_check;
+    off for prefill, whose PV product takes the softmax weights as bf16, which
+    moves an output by up to 2^-9 of its V spread).
+    """
     g = tensors.bf16_to_f64(got) if got.dtype == torch.bfloat16 else got.detach().double().cpu().numpy()
     assert g.shape == ref.shape, (g.shape, ref.shape)
     assert np.all(np.isfinite(g)), f"{what}: non-finite output"
@@ -37,5 +44,9 @@ def assert_close(got: torch.Tensor, ref: np.ndarray, what: str, atol=ATOL, rtol=
         idx = np.unravel_index(np.argmax(err - (atol + rtol * np.abs(ref))), err.shape)
         msg += f" worst at {idx}: got {g[idx]} ref {ref[idx]}"
     assert not bad.any(), msg
-    assert err.max() <= atol, msg
+    if ulp_check and got.dtype == torch.bfloat16:
+        _, e = np.frexp(ref)
+        ulp = np.ldexp(1.0, np.maximum(e - 1, -126) - 7)   # bf16 spacing at |ref|
+        over = err - (ulp + 2e-3 * np.maximum(1.0, np.abs(ref)))
+        assert not (over > 0).any(), f"{what}: error above one bf16 ulp (+2e-3 rel) at {int((over > 0).sum())} elements; {msg}"
     return float(err.max()), max_rel

@@ -115,7 +115,7 @@ def test_decode_flat_table_and_strided_views():
     oview = obig[:, 1:Hq + 1, :D]
     ws = tensors.decode_workspace(B, Hq, D, DEV)
     lse_big = torch.full((B, Hq + 5), float("nan"), dtype=torch.float32, device=DEV)
-    tensors.run_decode(dev, o=oview, lse=lse_big[:, :Hq], workspace=ws)
+    tensors.run_decode(dev, o=oview, lse=lse_big[:, :Hq], workspace=ws, num_splits=4)
     torch.cuda.synchronize()
     assert torch.equal(oview.contiguous().view(torch.int16), o_flat.view(torch.int16))
     assert torch.isnan(obig[:, 0]).all() and torch.isnan(obig[:, Hq + 1:]).all() and torch.isnan(obig[:, :, D:]).all()
