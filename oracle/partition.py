@@ -50,7 +50,7 @@ import numpy as np
 from .attention import attention_over_range, bf16_bits_to_f64, request_slots
 
 DEFAULTS = {
-    "wg_per_cu": 2,        # work groups per compute unit the plan aims for
+    "wg_per_cu": 3,        # work groups per compute unit the plan aims for
     "min_tokens": 64,      # fewest keys per work group on average
     "max_splits": 256,     # cap on work groups per kv head
 }

@@ -68,6 +68,9 @@ def load_library(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m paged_gqa_decode_astr_amd.build` "
                            "(there is no fallback implementation)")
+    # Load torch's HIP runtime first so the process holds a single libamdhip64
+    # (ours resolves to the already-loaded copy by soname).
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     lib.astr_workspace_size.restype = ctypes.c_size_t
     lib.astr_workspace_size.argtypes = [ctypes.c_int32] * 4

@@ -35,8 +35,10 @@ int ok() {
   return ASTR_OK;
 }
 
-// Planner constants (work groups per CU, fewest keys per work group, cap).
-constexpr int64_t kWgPerCu = 2;
+// Planner constants: work groups per CU (three 4-wavefront work groups fill
+// a CU at the head_dim-128 kernel's register budget), fewest keys per work
+// group on average (one 16-key tile for each of its wavefronts).
+constexpr int64_t kWgPerCu = 3;
 constexpr int64_t kMinTokens = 64;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -123,6 +125,13 @@ int validate_common(const astr_paged_args* a, bool prefill, int64_t* total_keys)
   }
   *total_keys = kv[a->batch];
   return ASTR_OK;
+}
+
+// Whether every byte offset of a pool row from its kv-head base,
+// slot * kv_stride_slot * 2 + head_dim * 2, stays below 2^32.
+bool pool_offsets_fit_32(const astr_paged_args* a) {
+  const int64_t last = (a->num_slots - 1) * a->kv_stride_slot * 2 + (int64_t)a->head_dim * 2;
+  return last < ((int64_t)1 << 32);
 }
 
 // Records timing_events[i] on the stream when the caller asked for it.
@@ -232,6 +241,7 @@ int astr_paged_decode(const astr_paged_args* a, void* workspace, size_t workspac
   p.req_to_token = a->req_to_token;
   p.req_to_token_stride = a->req_to_token_stride;
   p.kv_indptr = a->kv_indptr;
+  p.off32 = pool_offsets_fit_32(a);
   p.num_splits = plan.num_splits;
   p.num_partials = plan.num_partials;
   p.o_part = static_cast<float*>(workspace);

@@ -17,23 +17,27 @@
 // fixed grid stays valid when sequence lengths change.
 //
 // Inside a work group, 4 wavefronts take interleaved 16-key tiles of a piece.
-// Per tile and wavefront:
-//  * K is fetched in the B-operand layout of v_mfma_f32_16x16x32_bf16 (lane
-//    l holds 8 bf16 of key l % 16; four lanes cover 64 contiguous bytes of a
-//    row per load), and the logits of all G query heads of the GQA group come
-//    out of D/32 MFMAs whose A operand repeats the group's q rows, so every
-//    lane receives the G logits of its own key.  Each K/V row is read from HBM
-//    once for all G heads.
-//  * V is fetched row-wise (D/8 lanes per 2D-byte row) and P.V runs on the
-//    VALU in fp32; the softmax weights cross from the MFMA layout to the row
-//    layout through a small wavefront-private LDS buffer.
-//  * The next tile's K/V loads and the slot ids two tiles ahead are issued
-//    before the current tile is computed (register double buffering).
+// Per tile and wavefront both products run on the matrix cores:
+//  * S^T = K Q^T with v_mfma_f32_16x16x32_bf16: A is the K tile as loaded
+//    (lane l holds 8 bf16 of key l % 16; four lanes cover 64 contiguous bytes
+//    of a row per load), B holds the group's q rows (column j is query head
+//    j % G), so every column of S^T is one head of the GQA group and each
+//    K/V row is read from HBM once for all G heads.  Lane l receives the
+//    logits of keys 4*(l/16)..+3 for head l % 16.
+//  * O^T += V^T P^T with v_mfma_f32_16x16x16_bf16: the weights, split into a
+//    bf16 high part and a bf16 remainder (two MFMAs, near-fp32 weights), are
+//    already in the B-operand layout; V^T comes from a wavefront-private LDS
+//    copy of the V tile through the transposing LDS read ds_read_b64_tr_b16
+//    (lane j of each 16-lane group addresses row 4*(l/16) + j/4, columns
+//    4*(j%4).. of a 16-column block and receives column j of rows
+//    4*(l/16)..+3).
+//  * K and V rows of a key share one slot id; the next tile's loads and the
+//    ids one tile further are issued before the current tile is computed.
 //  * Softmax runs in base 2 against a lazily raised reference max: the
 //    accumulators are rescaled only when a logit exceeds the reference by more
 //    than kTau (so weights stay <= 2^kTau); the exact running max is tracked
 //    alongside and the written (m, l) pair uses it.  Keys past the piece end
-//    are never read and weigh exactly zero.
+//    weigh exactly zero; their loads re-read a valid key of the same request.
 // At the end of a piece the 4 wavefronts merge through LDS and one normalised
 // partial (o, m, l) per query head is written.
 #include "device_common.hpp"
@@ -43,6 +47,9 @@ namespace astr {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 
 constexpr int kThreads = 256;
@@ -64,318 +71,456 @@ __device__ __forceinline__ int request_of(const int32_t* kv_indptr, int B, int64
   return count;
 }
 
-template <int D, int G>
+template <int D>
 struct Shape {
-  static constexpr int kSteps = D / 32;            // MFMA k-steps over the head dim
-  static constexpr int kPasses = (G + 3) / 4;      // MFMAs per k-step (4 heads per pass)
-  static constexpr int kLanesPerRow = D / 8;       // V row layout: lanes per head row
-  static constexpr int kRowsPerLoad = kWave / kLanesPerRow;
-  static constexpr int kVLoads = kTile / kRowsPerLoad;
+  static constexpr int kSteps = D / 32;    // 16-byte K (and V) loads per lane per tile; QK^T k-steps
+  static constexpr int kDBlocks = D / 16;  // 16-wide d blocks of O^T (PV MFMAs per tile)
+  static constexpr int kVRow = D + 16;     // LDS row stride of the V tile (elements), padded
 };
 
-template <int D, int G>
+// K and V of one 16-key tile in the MFMA A-operand layout: lane l holds the
+// 16-byte chunks 8*(l/16) + 32*s of key l % 16.
+template <int D>
 struct Tile {
-  uint4 k[Shape<D, G>::kSteps];
-  uint4 v[Shape<D, G>::kVLoads];
+  uint4 k[Shape<D>::kSteps];
+  uint4 v[Shape<D>::kSteps];
 };
 
-template <int D, int G>
-__device__ __forceinline__ void load_tile(Tile<D, G>& t, const DecodeLaunch& p, int id_k, int t0, int t_end,
-                                          int64_t head_off, int lane) {
-  using S = Shape<D, G>;
-  const int l16 = lane & 15;
-  const int kb = lane >> 4;
-  const int r = lane / S::kLanesPerRow;
-  const int c = lane % S::kLanesPerRow;
-  const bool kvalid = t0 + l16 < t_end;
-  const int64_t kbase = (int64_t)id_k * p.kv_stride_slot + head_off;
-#pragma unroll
-  for (int s = 0; s < S::kSteps; ++s)
-    t.k[s] = kvalid ? load16(p.k_pool + kbase + 32 * s + 8 * kb) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-  for (int i = 0; i < S::kVLoads; ++i) {
-    const int tok = r + S::kRowsPerLoad * i;                 // key within the tile
-    const int id_v = __shfl(id_k, tok, kWave);               // lane `tok` holds that key's slot
-    const bool vvalid = t0 + tok < t_end;
-    t.v[i] = vvalid ? load16(p.v_pool + (int64_t)id_v * p.kv_stride_slot + head_off + 8 * c) : make_uint4(0, 0, 0, 0);
+// Slot id of key t0 + l % 16.  Keys past the piece end are clamped to its last
+// key, so every load is unconditional: a branch around a load would keep the
+// compiler from counting outstanding loads, and it would then wait for the
+// prefetched tile before computing the current one.
+__device__ __forceinline__ int load_id(const int32_t* row, int t0, int t_end, int lane) {
+  return row[min(t0 + (lane & 15), t_end - 1)];
+}
+
+// Pool rows are addressed from a per-kv-head base (wavefront-uniform, so it
+// lives in scalar registers) plus a per-lane byte offset.  When every offset
+// fits in 32 bits (pools up to 4 GiB per kv-head stride range) the offset is
+// computed in 32-bit arithmetic and the loads use the scalar-base addressing
+// mode; larger pools take 64-bit offsets.
+template <bool OFF32>
+__device__ __forceinline__ uint4 load_row16(const char* base, int slot, int64_t row_bytes, int extra) {
+  if constexpr (OFF32) {
+    const uint32_t off = (uint32_t)slot * (uint32_t)row_bytes + (uint32_t)extra;
+    return *reinterpret_cast<const uint4*>(base + off);
+  } else {
+    return *reinterpret_cast<const uint4*>(base + (int64_t)slot * row_bytes + extra);
   }
 }
 
-template <int D, int G>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeLaunch p) {
-  using S = Shape<D, G>;
-  constexpr int LPR = S::kLanesPerRow;
-  constexpr int RPL = S::kRowsPerLoad;
-  constexpr int GP = (G + 3) / 4 * 4;   // p row padded to whole 16-byte vectors
+template <int D, bool OFF32>
+__device__ __forceinline__ void load_tile(Tile<D>& t, const char* kbase, const char* vbase, int64_t row_bytes, int id,
+                                          int lane) {
+  const int kb = lane >> 4;
+#pragma unroll
+  for (int s = 0; s < Shape<D>::kSteps; ++s) {
+    t.k[s] = load_row16<OFF32>(kbase, id, row_bytes, 16 * kb + 64 * s);
+    t.v[s] = load_row16<OFF32>(vbase, id, row_bytes, 16 * kb + 64 * s);
+  }
+}
+
+// The pieces of a work group (requests its key range touches).  kv_indptr is
+// staged in LDS in windows of kKvStage entries (normally the whole array, in
+// one round trip); pieces are processed in batches that fit the window.
+// Piece j of a batch is request b0 + j; its keys inside the range are
+// positions [t_begin(j), t_end(j)) of that request.
+constexpr int kKvStage = 1024;
+
+struct PieceTable {
+  const int32_t* kv;   // LDS copy of kv_indptr[b0 .. b0 + n]
+  int64_t e0, e1;      // the work group's flat key range
+  int b0, n;
+  __device__ __forceinline__ int t_begin(int j) const { return (int)(max(e0, (int64_t)kv[j]) - kv[j]); }
+  __device__ __forceinline__ int t_end(int j) const { return (int)(min(e1, (int64_t)kv[j + 1]) - kv[j]); }
+};
+
+// A wavefront's position in its sequence of tiles: piece j, first key t of
+// the tile.  Wavefront wv takes tiles t_begin + kTile * (wv + kWaves * k) of
+// every piece, k = 0 .. nk - 1, with nk rounded up to an even count (the pad
+// tile is fully masked), so that tiles always come in pairs within a piece;
+// `stop` is the padded end.  j == n marks the end of the sequence.
+struct Cursor {
+  int j, t, stop;
+};
+
+__device__ __forceinline__ void settle(Cursor& c, const PieceTable& pt, int wv) {
+  while (c.j < pt.n) {
+    const int tb = pt.t_begin(c.j) + kTile * wv;
+    const int te = pt.t_end(c.j);
+    if (tb < te) {
+      int nk = (te - tb + kWaves * kTile - 1) / (kWaves * kTile);
+      nk += nk & 1;
+      c.t = tb;
+      c.stop = tb + nk * kWaves * kTile;
+      return;
+    }
+    ++c.j;
+  }
+}
+
+__device__ __forceinline__ void advance(Cursor& c, const PieceTable& pt, int wv) {
+  if (c.j >= pt.n) return;
+  c.t += kWaves * kTile;
+  if (c.t < c.stop) return;
+  ++c.j;
+  settle(c, pt, wv);
+}
+
+template <int D, int G, bool OFF32>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void decode_split_kernel(const DecodeLaunch p) {
+  using S = Shape<D>;
+  constexpr int NS = S::kSteps;
+  constexpr int NB = S::kDBlocks;
+  constexpr int QSTR = D + 8;   // padded q row (spreads LDS banks)
   __shared__ float sm_acc[kWaves][G][D];
   __shared__ float sm_mref[kWaves][G];
   __shared__ float sm_mx[kWaves][G];
   __shared__ float sm_l[kWaves][G];
-  __shared__ __align__(16) float sm_p[kWaves][kTile][GP];
+  __shared__ __align__(16) uint16_t sm_q[2][G][QSTR];            // q rows of the current / next piece
+  __shared__ __align__(16) uint16_t sm_v[kWaves][kTile][S::kVRow];  // per-wavefront V tile
+  __shared__ int32_t sm_kv[kKvStage];                              // window of kv_indptr starting at kv_base
 
   const int w = blockIdx.x;
   const int g = blockIdx.y;
   const int B = p.batch;
-  const int64_t N = p.kv_indptr[B];
-  const int64_t W = min((int64_t)p.num_splits, N);
-  if (w >= W) return;  // uniform over the work group
-  const int64_t e0 = ((int64_t)w * N) / W;
-  const int64_t e1 = ((int64_t)(w + 1) * N) / W;
-
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wv = tid / kWave;
+  const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);   // wavefront-uniform
   const int l16 = lane & 15;
   const int kb = lane >> 4;
-  const int r = lane / LPR;
-  const int c = lane % LPR;
+  const int hcol = l16 % G;     // query head of this lane's S^T / O^T column
   const float qscale = p.sm_scale * kLog2e;
-  const int64_t head_off = (int64_t)g * p.kv_stride_head;
-  constexpr int kStep = kWaves * kTile;   // keys between a wavefront's consecutive tiles
+  const char* kbase = reinterpret_cast<const char*>(p.k_pool + (int64_t)g * p.kv_stride_head);
+  const char* vbase = reinterpret_cast<const char*>(p.v_pool + (int64_t)g * p.kv_stride_head);
+  const int64_t row_bytes = p.kv_stride_slot * 2;
 
-  int b = request_of(p.kv_indptr, B, e0);
-  for (; b < B; ++b) {
-    const int64_t kb0 = p.kv_indptr[b];
-    const int64_t kb1 = p.kv_indptr[b + 1];
-    if (kb0 >= e1) break;
-    const int t_begin = (int)(max(e0, kb0) - kb0);
-    const int t_end = (int)(min(e1, kb1) - kb0);
-    const int32_t* ids = p.req_to_token + (p.req_to_token_stride > 0 ? (int64_t)b * p.req_to_token_stride : kb0);
+  // kv_indptr[0 .. min(B, kKvStage - 1)] -> LDS in one round trip.
+  int kv_base = 0;
+  const int staged = min(B, kKvStage - 1);
+  for (int t = tid; t <= staged; t += kThreads) sm_kv[t] = p.kv_indptr[t];
+  const int64_t N_glob = B > staged ? (int64_t)p.kv_indptr[B] : 0;
+  __syncthreads();
+  const int64_t N = B > staged ? N_glob : (int64_t)sm_kv[B];
+  const int64_t W = min((int64_t)p.num_splits, N);
+  if (w >= W) return;  // uniform over the work group
 
-    // Slot ids (MFMA layout: lane l <-> key l % 16) and K/V of the first tile.
-    int tile0 = t_begin + wv * kTile;
-    int id_cur = (tile0 + l16 < t_end) ? ids[tile0 + l16] : 0;
-    int id_next = (tile0 + kStep + l16 < t_end) ? ids[tile0 + kStep + l16] : 0;
-    Tile<D, G> cur, nxt;
-    if (tile0 < t_end) load_tile<D, G>(cur, p, id_cur, tile0, t_end, head_off, lane);
-
-    // A operand: row i of pass ps is query head (4 ps + i % 4) % G of the group.
-    bf16x8 qa[S::kPasses][S::kSteps];
-#pragma unroll
-    for (int ps = 0; ps < S::kPasses; ++ps) {
-      const int hh = (4 * ps + (l16 & 3)) % G;
-      const uint16_t* qrow = p.q + (int64_t)b * p.q_stride_tok + (int64_t)(g * G + hh) * p.q_stride_head;
-#pragma unroll
-      for (int s = 0; s < S::kSteps; ++s) qa[ps][s] = __builtin_bit_cast(bf16x8, load16(qrow + 32 * s + 8 * kb));
+  PieceTable pt;
+  pt.e0 = ((int64_t)w * N) / W;
+  pt.e1 = ((int64_t)(w + 1) * N) / W;
+  int bnext;
+  if (B <= staged) {
+    // Largest b < B with kv_indptr[b] <= e0 (binary search in LDS).
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((int64_t)sm_kv[mid] <= pt.e0) lo = mid; else hi = mid - 1;
     }
+    bnext = lo;
+  } else {
+    bnext = request_of(p.kv_indptr, B, pt.e0);
+  }
 
-    float mref[G], mx[G], lsum[G], acc[G][8];
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      mref[hh] = -INFINITY;
-      mx[hh] = -INFINITY;
-      lsum[hh] = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
+  for (;;) {
+    // Keep the window holding kv_indptr[bnext] and at least one entry after it.
+    if (bnext - kv_base + 1 >= kKvStage) {
+      __syncthreads();
+      kv_base = bnext;
+      for (int t = tid; t < kKvStage; t += kThreads) sm_kv[t] = p.kv_indptr[min(kv_base + t, B)];
+      __syncthreads();
     }
+    if (bnext >= B || (int64_t)sm_kv[bnext - kv_base] >= pt.e1) break;
+    pt.b0 = bnext;
+    pt.kv = sm_kv + (bnext - kv_base);
+    const int room = kKvStage - 1 - (bnext - kv_base);
+    int n = 0;
+    while (n < room && pt.b0 + n < B && (int64_t)pt.kv[n] < pt.e1) ++n;
+    pt.n = n;
+    bnext = pt.b0 + n;
 
-    for (; tile0 < t_end; tile0 += kStep) {
-      const int tnext = tile0 + kStep;
-      if (tnext < t_end) load_tile<D, G>(nxt, p, id_next, tnext, t_end, head_off, lane);
-      const int tnn = tnext + kStep;
-      const int id_nn = (tnn + l16 < t_end) ? ids[tnn + l16] : 0;
+    // Slot id of the tile at cursor cu for this lane's key (a past-the-end
+    // cursor re-reads the last key of the last piece; its data is never used).
+    auto id_at = [&](const Cursor& cu) -> int {
+      const int j = min(cu.j, pt.n - 1);
+      const int t_end = pt.t_end(j);
+      const int t0 = cu.j < pt.n ? cu.t : t_end - 1;
+      const int32_t* row = p.req_to_token + (p.req_to_token_stride > 0 ? (int64_t)(pt.b0 + j) * p.req_to_token_stride
+                                                                        : (int64_t)pt.kv[j]);
+      return load_id(row, t0, t_end, lane);
+    };
+    // q rows of piece j's request: 16 bytes per thread for the first G*D/8 threads.
+    constexpr int kQThreads = G * D / 8;
+    auto q_chunk = [&](int j) -> uint4 {
+      const int t = min(tid, kQThreads - 1);
+      const int hh = t / (D / 8), dc = t % (D / 8);
+      return load16(p.q + (int64_t)(pt.b0 + j) * p.q_stride_tok + (int64_t)(g * G + hh) * p.q_stride_head + 8 * dc);
+    };
+    auto q_store = [&](int buf, const uint4& v) {
+      if (tid < kQThreads) *reinterpret_cast<uint4*>(&sm_q[buf][tid / (D / 8)][8 * (tid % (D / 8))]) = v;
+    };
 
-      // Logits of key l16 for every head of the group, in log2 units.
-      float sc[G];
+    // Ping-pong pipeline over the wavefront's tile sequence c0, c1, c2, ...
+    // (which runs across piece boundaries).  While tile k is computed from
+    // one register buffer, tile k+1 is in flight into the other; right after,
+    // the first buffer is refilled with tile k+2.  Slot ids run one tile
+    // further ahead and are always issued before the data loads that must
+    // stay in flight while they are used: vmcnt retires loads in issue order,
+    // so an id load issued after a data load could only be waited for
+    // together with it.  Tiles come in pairs within a piece, so buffer A
+    // always holds even tiles and B odd ones and no register copy (which
+    // would wait for its load) is ever needed.
+    Cursor c0{0, 0, 0};
+    settle(c0, pt, wv);
+    Cursor c1 = c0;
+    advance(c1, pt, wv);
+    Cursor c2 = c1;
+    advance(c2, pt, wv);
+    Cursor c3 = c2;
+    advance(c3, pt, wv);
+    const uint4 q_first = q_chunk(0);
+    int iA = id_at(c0);
+    int iB = id_at(c1);
+    Tile<D> A, Bt;
+    load_tile<D, OFF32>(A, kbase, vbase, row_bytes, iA, lane);
+    iA = id_at(c2);
+    load_tile<D, OFF32>(Bt, kbase, vbase, row_bytes, iB, lane);
+    q_store(0, q_first);
+    __syncthreads();
+
+    float mref = -INFINITY, mx = -INFINITY, lsum = 0.f;
+    f32x4 acc[NB];
+    bf16x8 qop[NS];
+    int t_end = 0;
+    uint16_t* vt = &sm_v[wv][0][0];
+
+    // Logits, softmax weights and P.V for the tile in buffer X (cursor c0).
+    auto compute = [&](const Tile<D>& X) {
+      f32x4 st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ps = 0; ps < S::kPasses; ++ps) {
-        f32x4 st = {0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < NS; ++s)
+        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, X.k[s]), qop[s], st, 0, 0, 0);
+      // st[r] = S^T[key 4 kb + r][head hcol]; V tile -> LDS meanwhile.
 #pragma unroll
-        for (int s = 0; s < S::kSteps; ++s) st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ps][s], __builtin_bit_cast(bf16x8, cur.k[s]), st, 0, 0, 0);
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (4 * ps + q < G) sc[4 * ps + q] = st[q] * qscale;
-      }
-      const bool kvalid = tile0 + l16 < t_end;
+      for (int s = 0; s < NS; ++s) *reinterpret_cast<uint4*>(vt + l16 * S::kVRow + 32 * s + 8 * kb) = X.v[s];
+      float sc[4];
+      float tmax = -INFINITY;
       bool raise = false;
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        if (!kvalid) sc[hh] = -INFINITY;
-        mx[hh] = fmaxf(mx[hh], sc[hh]);
-        raise |= sc[hh] > mref[hh] + kTau;
+      for (int r = 0; r < 4; ++r) {
+        sc[r] = (c0.t + 4 * kb + r < t_end) ? st[r] * qscale : -INFINITY;
+        tmax = fmaxf(tmax, sc[r]);
+        raise |= sc[r] > mref + kTau;
       }
+      mx = fmaxf(mx, tmax);
       if (__builtin_amdgcn_ballot_w64(raise) != 0) {   // uniform over the wavefront
+        const float mnew = fmaxf(mref, xor_max<16, kWave>(tmax));
+        const float alpha = exp2f(mref - mnew);
+        mref = mnew;
+        lsum *= alpha;
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-          const float tmax = xor_max<1, 16>(sc[hh]);
-          const float mnew = fmaxf(mref[hh], tmax);
-          const float alpha = exp2f(mref[hh] - mnew);
-          mref[hh] = mnew;
-          lsum[hh] *= alpha;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[hh][e] *= alpha;
-        }
+        for (int b = 0; b < NB; ++b) acc[b] *= alpha;
       }
-      // Weights to the row layout through LDS (wavefront-private buffer).
-      if (lane < kTile) {
-        float pw[GP];
+      // Weights as a bf16 high part plus a bf16 remainder for two P.V MFMAs
+      // (about 16 significant bits); the sum uses the fp32 weights.
+      bf16x4 phi, plo;
 #pragma unroll
-        for (int hh = 0; hh < GP; ++hh) pw[hh] = hh < G ? exp2f(sc[hh] - mref[hh]) : 0.f;
-#pragma unroll
-        for (int v4 = 0; v4 < GP / 4; ++v4)
-          *reinterpret_cast<float4*>(&sm_p[wv][lane][4 * v4]) = make_float4(pw[4 * v4], pw[4 * v4 + 1], pw[4 * v4 + 2], pw[4 * v4 + 3]);
+      for (int r = 0; r < 4; ++r) {
+        const float pr = __builtin_amdgcn_exp2f(sc[r] - mref);
+        lsum += pr;
+        phi[r] = (__bf16)pr;
+        plo[r] = (__bf16)(pr - (float)phi[r]);
       }
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
-      for (int i = 0; i < S::kVLoads; ++i) {
-        const int tok = r + RPL * i;
-        float pw[GP];
-#pragma unroll
-        for (int v4 = 0; v4 < GP / 4; ++v4) {
-          const float4 x = *reinterpret_cast<const float4*>(&sm_p[wv][tok][4 * v4]);
-          pw[4 * v4] = x.x; pw[4 * v4 + 1] = x.y; pw[4 * v4 + 2] = x.z; pw[4 * v4 + 3] = x.w;
-        }
-        float vf[8];
-        unpack8(cur.v[i], vf);
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-          lsum[hh] += pw[hh];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[hh][e] = fmaf(pw[hh], vf[e], acc[hh][e]);
-        }
+      for (int b = 0; b < NB; ++b) {
+        const s16x4 av = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(vt + (4 * kb + (l16 >> 2)) * S::kVRow + 16 * b + 4 * (l16 & 3)));
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, __builtin_bit_cast(s16x4, phi), acc[b], 0, 0, 0);
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, __builtin_bit_cast(s16x4, plo), acc[b], 0, 0, 0);
       }
       __builtin_amdgcn_wave_barrier();
-      cur = nxt;
-      id_next = id_nn;
-    }
+    };
+    // One pipeline step: X holds tile c0, the other buffer holds c1 (in
+    // flight), iX holds the id of c2; iY is free and receives the id of c3.
+    auto step = [&](Tile<D>& X, int& iX, int& iY) {
+      compute(X);
+      iY = id_at(c3);
+      load_tile<D, OFF32>(X, kbase, vbase, row_bytes, iX, lane);
+      c0 = c1;
+      c1 = c2;
+      c2 = c3;
+      advance(c3, pt, wv);
+    };
 
-    // Wavefront totals: rows of the V layout, and the exact max over keys.
+    for (int j = 0; j < pt.n; ++j) {
+      const uint4 q_next = q_chunk(min(j + 1, pt.n - 1));
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      lsum[hh] = xor_sum<LPR, kWave>(lsum[hh]);
-      mx[hh] = xor_max<1, 16>(mx[hh]);
+      for (int s = 0; s < NS; ++s) qop[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&sm_q[j & 1][hcol][32 * s + 8 * kb]));
+      mref = -INFINITY;
+      mx = -INFINITY;
+      lsum = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[hh][e] = xor_sum<LPR, kWave>(acc[hh][e]);
-    }
-    if (r == 0) {
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sm_acc[wv][hh][c * 8 + e] = acc[hh][e];
-    }
-    if (lane == 0) {
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        sm_mref[wv][hh] = mref[hh];
-        sm_mx[wv][hh] = mx[hh];
-        sm_l[wv][hh] = lsum[hh];
+      for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+      t_end = pt.t_end(j);
+      while (c0.j == j) {
+        step(A, iA, iB);
+        step(Bt, iB, iA);
       }
-    }
-    __syncthreads();
-    const int slot = w + b;
-    for (int idx = tid; idx < G * D; idx += kThreads) {
-      const int hh = idx / D;
-      const int d = idx % D;
-      float M = -INFINITY;
+
+      // Wavefront totals over the four key groups of each column.
+      lsum = xor_sum<16, kWave>(lsum);
+      mx = xor_max<16, kWave>(mx);
+      if (l16 < G) {
 #pragma unroll
-      for (int k = 0; k < kWaves; ++k) M = fmaxf(M, sm_mx[k][hh]);
-      float num = 0.f, den = 0.f;
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int k = 0; k < kWaves; ++k) {
-        if (sm_mref[k][hh] == -INFINITY) continue;  // wavefront had no key of this piece
-        const float sc = exp2f(sm_mref[k][hh] - M);
-        num = fmaf(sm_acc[k][hh][d], sc, num);
-        den = fmaf(sm_l[k][hh], sc, den);
+          for (int r = 0; r < 4; ++r) sm_acc[wv][l16][16 * b + 4 * kb + r] = acc[b][r];
+        if (kb == 0) {
+          sm_mref[wv][l16] = mref;
+          sm_mx[wv][l16] = mx;
+          sm_l[wv][l16] = lsum;
+        }
       }
-      const int64_t pidx = (int64_t)(g * G + hh) * p.num_partials + slot;
-      p.o_part[pidx * D + d] = num / den;
-      if (d == 0) {
-        p.ml_part[pidx * 2 + 0] = M * kLn2;
-        p.ml_part[pidx * 2 + 1] = den;
+      q_store((j + 1) & 1, q_next);   // buffer last used by piece j - 1
+      __syncthreads();
+      const int slot = w + pt.b0 + j;
+      for (int idx = tid; idx < G * D; idx += kThreads) {
+        const int hh = idx / D;
+        const int d = idx % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < kWaves; ++k) M = fmaxf(M, sm_mx[k][hh]);
+        float num = 0.f, den = 0.f;
+#pragma unroll
+        for (int k = 0; k < kWaves; ++k) {
+          if (sm_mref[k][hh] == -INFINITY) continue;  // wavefront had no key of this piece
+          const float sc = exp2f(sm_mref[k][hh] - M);
+          num = fmaf(sm_acc[k][hh][d], sc, num);
+          den = fmaf(sm_l[k][hh], sc, den);
+        }
+        const int64_t pidx = (int64_t)(g * G + hh) * p.num_partials + slot;
+        p.o_part[pidx * D + d] = num / den;
+        if (d == 0) {
+          p.ml_part[pidx * 2 + 0] = M * kLn2;
+          p.ml_part[pidx * 2 + 1] = den;
+        }
       }
+      __syncthreads();
     }
-    __syncthreads();
   }
 }
 
 // One work group per (request, kv head): merges the pieces w_first..w_last
-// of the request for the G query heads of kv head g.  Pass 1: one wavefront
-// per head reduces the max logit M and the total weight sum_s l_s e^(m_s - M).
-// Pass 2: the weights of up to kChunk pieces are staged in LDS and every
-// thread accumulates its (head, d) outputs with independent loads.
-constexpr int kChunk = 64;
+// of the request for the G query heads of kv head g.  kGroups thread groups
+// take interleaved pieces; each thread folds its pieces into (M, den, num)
+// for its (head, d) outputs with an online log-sum-exp merge, kBatch pieces
+// at a time so their loads are in flight together; the groups then merge
+// through LDS.
+constexpr int kBatch = 8;
+constexpr int kGroups = 4;
+constexpr int kCombineThreads = kThreads * kGroups;
 
 template <int D, int G>
-__global__ __launch_bounds__(kThreads) void decode_combine_kernel(const DecodeLaunch p) {
+__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const DecodeLaunch p) {
   constexpr int kPer = (G * D + kThreads - 1) / kThreads;   // outputs per thread
-  __shared__ float s_w[G][kChunk];
-  __shared__ float s_M[G];
-  __shared__ float s_den[G];
+  __shared__ float s_part[kGroups - 1][3][kPer][kThreads];
   const int b = blockIdx.x;
   const int g = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wv = tid / kWave;
+  const int tid = threadIdx.x % kThreads;
+  const int grp = threadIdx.x / kThreads;
   const int64_t N = p.kv_indptr[p.batch];
-  const int64_t W = min((int64_t)p.num_splits, N);
   const int64_t x0 = p.kv_indptr[b];
   const int64_t x1 = (int64_t)p.kv_indptr[b + 1] - 1;
+  const int64_t W = min((int64_t)p.num_splits, N);
   const int wf = (int)(((x0 + 1) * W + N - 1) / N - 1);
   const int wl = (int)(((x1 + 1) * W + N - 1) / N - 1);
   const int n = wl - wf + 1;
-
-  for (int hh = wv; hh < G; hh += kWaves) {
-    const float* ml = p.ml_part + ((int64_t)(g * G + hh) * p.num_partials + b + wf) * 2;
-    float M = -INFINITY;
-    for (int i = lane; i < n; i += kWave) M = fmaxf(M, ml[2 * i]);
-    M = xor_max<1, kWave>(M);
-    float den = 0.f;
-    for (int i = lane; i < n; i += kWave) den += ml[2 * i + 1] * expf(ml[2 * i] - M);
-    den = xor_sum<1, kWave>(den);
-    if (lane == 0) {
-      s_M[hh] = M;
-      s_den[hh] = den;
-    }
-  }
-  __syncthreads();
-
-  float num[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) num[j] = 0.f;
-  for (int c0 = 0; c0 < n; c0 += kChunk) {
-    const int cn = min(kChunk, n - c0);
-    for (int idx = tid; idx < G * kChunk; idx += kThreads) {
-      const int hh = idx / kChunk, i = idx % kChunk;
-      if (i < cn) {
-        const float* ml = p.ml_part + ((int64_t)(g * G + hh) * p.num_partials + b + wf + c0 + i) * 2;
-        s_w[hh][i] = ml[1] * expf(ml[0] - s_M[hh]);
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int idx = tid + j * kThreads;
-      if (idx < G * D) {
-        const int hh = idx / D, d = idx % D;
-        const float* op = p.o_part + ((int64_t)(g * G + hh) * p.num_partials + b + wf + c0) * D + d;
-        float a = num[j];
-        for (int i = 0; i < cn; ++i) a = fmaf(s_w[hh][i], op[(int64_t)i * D], a);
-        num[j] = a;
-      }
-    }
-    __syncthreads();
-  }
+  float Ms[kPer], dens[kPer], nums[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int idx = tid + j * kThreads;
+    float M = -INFINITY, den = 0.f, num = 0.f;
     if (idx < G * D) {
       const int hh = idx / D, d = idx % D;
-      const int h = g * G + hh;
-      p.o[(int64_t)b * p.o_stride_tok + (int64_t)h * p.o_stride_head + d] = f32_to_bf16_rne(num[j] / s_den[hh]);
-      if (p.lse != nullptr && d == 0) p.lse[(int64_t)b * p.lse_stride_tok + h] = s_M[hh] + logf(s_den[hh]);
+      const int64_t base = (int64_t)(g * G + hh) * p.num_partials + b + wf;
+      const float* ml = p.ml_part + base * 2;
+      const float* op = p.o_part + base * D + d;
+      for (int i0 = grp; i0 < n; i0 += kBatch * kGroups) {
+        float m[kBatch], l[kBatch], o[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+          const int pi = min(i0 + i * kGroups, n - 1);
+          m[i] = ml[2 * pi];
+          l[i] = ml[2 * pi + 1];
+          o[i] = op[(int64_t)pi * D];
+        }
+        float Mb = M;
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i)
+          if (i0 + i * kGroups < n) Mb = fmaxf(Mb, m[i]);
+        const float sc = expf(M - Mb);   // M == -inf on the first batch: scales zeros
+        den *= sc;
+        num *= sc;
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+          if (i0 + i * kGroups >= n) continue;
+          const float wgt = l[i] * expf(m[i] - Mb);
+          den += wgt;
+          num = fmaf(wgt, o[i], num);
+        }
+        M = Mb;
+      }
     }
+    Ms[j] = M;
+    dens[j] = den;
+    nums[j] = num;
+  }
+  if (grp > 0) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      s_part[grp - 1][0][j][tid] = Ms[j];
+      s_part[grp - 1][1][j][tid] = dens[j];
+      s_part[grp - 1][2][j][tid] = nums[j];
+    }
+  }
+  __syncthreads();
+  if (grp > 0) return;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int idx = tid + j * kThreads;
+    if (idx >= G * D) break;
+    float M = Ms[j];
+#pragma unroll
+    for (int k = 0; k < kGroups - 1; ++k) M = fmaxf(M, s_part[k][0][j][tid]);
+    float den = dens[j] * expf(Ms[j] - M);   // group 0 always holds piece 0: Ms[j] is finite
+    float num = nums[j] * expf(Ms[j] - M);
+#pragma unroll
+    for (int k = 0; k < kGroups - 1; ++k) {
+      const float mk = s_part[k][0][j][tid];
+      if (mk == -INFINITY) continue;   // group had no piece
+      const float sc = expf(mk - M);
+      den = fmaf(s_part[k][1][j][tid], sc, den);
+      num = fmaf(s_part[k][2][j][tid], sc, num);
+    }
+    const int hh = idx / D, d = idx % D;
+    const int h = g * G + hh;
+    p.o[(int64_t)b * p.o_stride_tok + (int64_t)h * p.o_stride_head + d] = f32_to_bf16_rne(num / den);
+    if (p.lse != nullptr && d == 0) p.lse[(int64_t)b * p.lse_stride_tok + h] = M + logf(den);
   }
 }
 
 template <int D, int G>
 hipError_t launch_split_t(const DecodeLaunch& p, hipStream_t s) {
-  hipLaunchKernelGGL((decode_split_kernel<D, G>), dim3(p.num_splits, p.num_kv_heads, 1), dim3(kThreads), 0, s, p);
+  if (p.off32)
+    hipLaunchKernelGGL((decode_split_kernel<D, G, true>), dim3(p.num_splits, p.num_kv_heads, 1), dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<D, G, false>), dim3(p.num_splits, p.num_kv_heads, 1), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
 template <int D, int G>
 hipError_t launch_combine_t(const DecodeLaunch& p, hipStream_t s) {
-  hipLaunchKernelGGL((decode_combine_kernel<D, G>), dim3(p.batch, p.num_kv_heads, 1), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL((decode_combine_kernel<D, G>), dim3(p.batch, p.num_kv_heads, 1), dim3(kCombineThreads), 0, s, p);
   return hipGetLastError();
 }
 

@@ -22,6 +22,7 @@ struct DecodeLaunch {
   const int32_t* req_to_token;
   int64_t req_to_token_stride;
   const int32_t* kv_indptr;
+  bool off32;            // every pool row offset from a kv-head base fits in 32 bits
   int32_t num_splits;    // Wh: work groups per kv head (grid.x)
   int32_t num_partials;  // P = Wh + B - 1 slots per query head
   float* o_part;         // [Hq][P][D]

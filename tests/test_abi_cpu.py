@@ -68,7 +68,7 @@ def test_plan_matches_oracle_random():
 
 def test_plan_config_examples():
     from paged_gqa_decode_astr_amd.workloads import make_inputs
-    for cid, want in [("tiny", None), ("decode_b32", 64)]:
+    for cid, want in [("tiny", None), ("decode_b32", 96)]:
         inp = make_inputs(cid, 0)
         a, keep = _args(inp["kv_indptr"], inp["num_qo_heads"], inp["num_kv_heads"], inp["head_dim"])
         plan = _lib.astr_plan_decode(a, 256)

@@ -348,9 +348,9 @@ def test_split_partials_only_planned_slots_written():
 
 
 def test_plan_num_splits_examples():
-    # 32 requests, 8 kv heads, 256 CUs: target ceil(2*256/8) = 64 work groups per kv head.
+    # 32 requests, 8 kv heads, 256 CUs: target ceil(3*256/8) = 96 work groups per kv head.
     kv = np.concatenate([[0], np.cumsum(np.full(32, 1100))])
-    assert oracle.plan_num_splits(kv, 8, 256) == 64
+    assert oracle.plan_num_splits(kv, 8, 256) == 96
     # Short batch: 130 keys in total -> ceil(130/64) = 3 work groups.
     assert oracle.plan_num_splits(np.array([0, 60, 130]), 1, 256) == 3
     # Single key -> one work group; forced value wins.
