@@ -13,8 +13,8 @@ are resident in HBM before the timed region starts.
 
 Prints one JSON line (stdout).  `value` is algorithmic HBM bytes of the whole
 call (K + V + Q + O + index arrays + lse) per second, in GB/s.  `roofline`
-is for the dominant kernel (the split kernel), timed live with HIP events the
-library records around each kernel on the launch stream.  `cpu_baseline`
+is for the dominant kernel (the split kernel), timed live with HIP events that
+the kernel's own dispatch stamps at its start and end (hipExtLaunchKernel).  `cpu_baseline`
 times the fp64 CPU oracle on the same workload.  `prefill` reports the ragged
 prefill kernel (B=8, prefix U{0..2048}, q_len U{1..512}) against the bf16
 MFMA peak.
@@ -40,25 +40,6 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def decode_bytes(inp, with_lse=True):
-    """Algorithmic bytes of one decode call, counted once."""
-    B, Hq, D = inp["q"].shape
-    Hkv = inp["num_kv_heads"]
-    N = int(inp["kv_indptr"][-1])
-    kv = N * Hkv * D * 2 * 2
-    qo = 2 * B * Hq * D * 2
-    idx = N * 4 + (B + 1) * 4
-    return kv + qo + idx + (B * Hq * 4 if with_lse else 0)
-
-
-def split_kernel_bytes(inp):
-    """Bytes the split kernel must read: K + V + Q + req_to_token entries + kv_indptr."""
-    B, Hq, D = inp["q"].shape
-    Hkv = inp["num_kv_heads"]
-    N = int(inp["kv_indptr"][-1])
-    return N * Hkv * D * 2 * 2 + B * Hq * D * 2 + N * 4 + (B + 1) * 4
-
-
 def prefill_flops(inp):
     """4 * D * Hq per visible (query row, key) pair; causally masked pairs are not counted."""
     _, Hq, D = inp["q"].shape
@@ -72,22 +53,9 @@ def prefill_flops(inp):
     return 4 * D * Hq * pairs
 
 
-def read_traffic(kernel_key):
-    """HBM traffic per launch from a committed rocprofv3 PMC summary, if it is for the current source."""
-    import hashlib
-    path = os.path.join(ROOT, "profiles", f"{kernel_key}_pmc.json")
-    if not os.path.exists(path):
-        return None
-    with open(path) as fh:
-        rec = json.load(fh)
-    src = os.path.join(ROOT, rec["source"])
-    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
-        return None
-    return rec.get("hbm_bytes_per_launch")
-
-
 def cpu_baseline(inp, budget_s):
     import oracle
+    from paged_gqa_decode_astr_amd import profiling
     from threadpoolctl import threadpool_limits
     with threadpool_limits(limits=1):
         runs, t0 = 0, time.perf_counter()
@@ -99,7 +67,7 @@ def cpu_baseline(inp, budget_s):
             if el >= budget_s:
                 break
     per = el / runs
-    return out, {"value": decode_bytes(inp) / per / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+    return out, {"value": profiling.decode_bytes(inp) / per / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
                  "sample": f"fp64 NumPy oracle over one full decode_b32 batch (set 0, {B_str(inp)}), "
                            f"{runs} run(s) in {el:.1f} s, {per * 1e3:.1f} ms/call, BLAS limited to 1 thread; "
                            f"host has {len(os.sched_getaffinity(0))} cores"}
@@ -128,7 +96,7 @@ def main(argv=None):
         return 2
 
     import torch
-    from paged_gqa_decode_astr_amd import _lib, tensors
+    from paged_gqa_decode_astr_amd import _lib, profiling, tensors
     from paged_gqa_decode_astr_amd.hip_events import HipEvent
     from paged_gqa_decode_astr_amd.workloads import CONFIGS, make_inputs
 
@@ -136,21 +104,11 @@ def main(argv=None):
     dev = "cuda"
     cfg = CONFIGS[args.config]
     log(f"[bench] building {args.sets} input sets of {args.config}")
-    sets = []
-    for t in range(args.sets):
-        inp = make_inputs(args.config, t)
-        d = tensors.to_device(inp, dev)
-        B, Hq, D = inp["q"].shape
-        d["o"] = torch.empty(B, Hq, D, dtype=torch.bfloat16, device=dev)
-        d["lse"] = torch.empty(B, Hq, dtype=torch.float32, device=dev)
-        d["ws"] = tensors.decode_workspace(B, Hq, D, dev, max_splits=args.num_splits)
-        sets.append((inp, d))
+    sets = tensors.decode_sets(args.config, args.sets, dev, num_splits=args.num_splits)
     torch.cuda.synchronize()
 
     def step(k, events=None):
-        _, d = sets[k % len(sets)]
-        tensors.run_decode(d, o=d["o"], lse=d["lse"], workspace=d["ws"], timing_events=events,
-                           num_splits=args.num_splits)
+        tensors.decode_step(sets, k, num_splits=args.num_splits, timing_events=events)
 
     log(f"[bench] warmup {args.warmup}")
     for k in range(args.warmup):
@@ -167,19 +125,19 @@ def main(argv=None):
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(stop)
     ms_per_step = ms_total / args.steps
-    total_bytes = sum(decode_bytes(sets[k % len(sets)][0]) for k in range(args.steps))
+    total_bytes = sum(profiling.decode_bytes(sets[k % len(sets)][0]) for k in range(args.steps))
     value = total_bytes / (ms_total * 1e-3) / 1e9
 
-    # Per-kernel durations: events recorded by the library around each kernel, same stream.
+    # Per-kernel durations: start/end stamps taken by each kernel's own dispatch (hipExtLaunchKernel).
     log("[bench] per-kernel event timing")
-    evs = [[HipEvent() for _ in range(3)] for _ in range(args.steps)]
+    evs = [[HipEvent() for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for k in range(args.steps):
         step(k, evs[k])
     torch.cuda.synchronize()
     split_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    comb_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
-    split_bytes = sum(split_kernel_bytes(sets[k % len(sets)][0]) for k in range(args.steps))
+    comb_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    split_bytes = sum(profiling.split_kernel_bytes(sets[k % len(sets)][0]) for k in range(args.steps))
     achieved = split_bytes / (split_ms.sum() * 1e-3) / 1e9
     plan = _lib.astr_plan_decode(_lib.make_args(
         sets[0][1]["q"], sets[0][1]["k_pool"], sets[0][1]["v_pool"], sets[0][1]["req_to_token"],
@@ -189,7 +147,7 @@ def main(argv=None):
     B, Hq, D = sets[0][0]["q"].shape
     G = Hq // cfg.num_kv_heads
     kernel_name = f"decode_split_kernel<{D},{G}>"
-    traffic = read_traffic(f"decode_split_{args.config}")
+    traffic = profiling.read_traffic(args.config)
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
@@ -219,7 +177,7 @@ def main(argv=None):
         psteps = max(10, args.steps // 4)
         pev = [[HipEvent() for _ in range(2)] for _ in range(psteps)]
         for k in range(psteps):
-            tensors.run_prefill(pd, o=po, lse=plse, timing_events=pev[k] + [None])
+            tensors.run_prefill(pd, o=po, lse=plse, timing_events=pev[k])
         torch.cuda.synchronize()
         pms = float(np.mean([e[0].elapsed_time(e[1]) for e in pev]))
         fl = prefill_flops(pin)

@@ -125,10 +125,13 @@ typedef struct astr_paged_args {
    * query-tile count for q_len up to this value (graph capture). */
   int32_t max_q_len;
 
-  /* Optional timing hook: NULL, or an array of hipEvent_t the call records on
-   * `stream`.  Decode records [0] before the split kernel, [1] between the
-   * split and combine kernels, [2] after the combine kernel.  Prefill records
-   * [0] before and [1] after its kernel.  Elements may be NULL (skipped). */
+  /* Optional timing hook: NULL, or an array of hipEvent_t (created with
+   * timing enabled) that the kernels' own dispatches stamp at kernel start
+   * and end (hipExtLaunchKernel), so that stop - start is one kernel's
+   * duration.  Decode: [0]/[1] start/end of the split kernel, [2]/[3]
+   * start/end of the combine kernel (4 entries).  Prefill: [0]/[1] (2
+   * entries).  Elements may be NULL (not stamped).  Events stay owned by the
+   * caller; leave this NULL in code that is captured into a graph. */
   void* const* timing_events;
 } astr_paged_args;
 

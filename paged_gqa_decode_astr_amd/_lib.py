@@ -164,7 +164,7 @@ def make_args(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host, o, *, 
     a.max_q_len = int(max_q_len)
     ev = None
     if timing_events is not None:
-        ev = (ctypes.c_void_p * 3)(*[None if e is None else e.cuda_event for e in timing_events])
+        ev = (ctypes.c_void_p * len(timing_events))(*[None if e is None else e.cuda_event for e in timing_events])
         a.timing_events = ctypes.cast(ev, ctypes.c_void_p)
     return a, (kvh, qoh, ev)
 
@@ -186,8 +186,10 @@ def astr_paged_decode(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host
                       sm_scale, req_to_token_stride, lse=None, num_splits=0, stream=None, timing_events=None):
     """Paged GQA decode: q [B, Hq, D] bf16 -> o [B, Hq, D] bf16 (+ lse [B, Hq] fp32).
 
-    timing_events: optional 3 torch.cuda.Event(enable_timing=True) recorded
-    before the split kernel, between split and combine, and after combine."""
+    timing_events: optional 4 HipEvent (hip_events.py): start/end stamps of the
+    split kernel, then of the combine kernel (None entries are skipped)."""
+    if timing_events is not None and len(timing_events) != 4:
+        raise ValueError("decode timing_events takes 4 events (split start/end, combine start/end)")
     lib = load_library()
     a, keep = make_args(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host, o, sm_scale=sm_scale,
                         req_to_token_stride=req_to_token_stride, lse=lse, num_splits=num_splits,
@@ -203,8 +205,10 @@ def astr_paged_prefill(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_hos
                        timing_events=None):
     """Ragged paged prefill: q [sum q_len, Hq, D] bf16 in qo_indptr order -> o (+ lse).
 
-    timing_events: optional 2 torch.cuda.Event(enable_timing=True) recorded
-    before and after the kernel."""
+    timing_events: optional 2 HipEvent (hip_events.py): start/end stamps of the
+    prefill kernel."""
+    if timing_events is not None and len(timing_events) != 2:
+        raise ValueError("prefill timing_events takes 2 events (kernel start/end)")
     lib = load_library()
     a, keep = make_args(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host, o, sm_scale=sm_scale,
                         req_to_token_stride=req_to_token_stride, lse=lse, qo_indptr=qo_indptr,

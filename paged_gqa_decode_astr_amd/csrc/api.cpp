@@ -134,12 +134,15 @@ bool pool_offsets_fit_32(const astr_paged_args* a) {
   return last < ((int64_t)1 << 32);
 }
 
-// Records timing_events[i] on the stream when the caller asked for it.
-int record_event(void* const* events, int i, hipStream_t s) {
-  if (events == nullptr || events[i] == nullptr) return ASTR_OK;
-  hipError_t e = hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
-  if (e != hipSuccess) return fail(ASTR_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
-  return ASTR_OK;
+// The caller's timing events i and i + 1 (either may be NULL) as the start
+// and end stamps of one kernel.
+astr::Timing timing_pair(void* const* events, int i) {
+  astr::Timing t;
+  if (events != nullptr) {
+    t.start = static_cast<hipEvent_t>(events[i]);
+    t.stop = static_cast<hipEvent_t>(events[i + 1]);
+  }
+  return t;
 }
 
 int plan_decode_impl(const astr_paged_args* a, int64_t total_keys, int32_t num_cus, astr_decode_plan* out) {
@@ -249,16 +252,10 @@ int astr_paged_decode(const astr_paged_args* a, void* workspace, size_t workspac
                                        align256((int64_t)a->num_qo_heads * plan.num_partials * a->head_dim * 4));
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  int st2 = record_event(a->timing_events, 0, s);
-  if (st2 != ASTR_OK) return st2;
-  hipError_t e = astr::launch_decode_split(p, s);
+  hipError_t e = astr::launch_decode_split(p, s, timing_pair(a->timing_events, 0));
   if (e != hipSuccess) return fail(ASTR_ERR_HIP, "split kernel launch: %s", hipGetErrorString(e));
-  st2 = record_event(a->timing_events, 1, s);
-  if (st2 != ASTR_OK) return st2;
-  e = astr::launch_decode_combine(p, s);
+  e = astr::launch_decode_combine(p, s, timing_pair(a->timing_events, 2));
   if (e != hipSuccess) return fail(ASTR_ERR_HIP, "combine kernel launch: %s", hipGetErrorString(e));
-  st2 = record_event(a->timing_events, 2, s);
-  if (st2 != ASTR_OK) return st2;
   return ok();
 }
 
@@ -315,12 +312,8 @@ int astr_paged_prefill(const astr_paged_args* a, void* workspace, size_t workspa
   p.qo_indptr = a->qo_indptr;
   p.max_q_len = max_q;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  st = record_event(a->timing_events, 0, s);
-  if (st != ASTR_OK) return st;
-  hipError_t e = astr::launch_prefill(p, s);
+  hipError_t e = astr::launch_prefill(p, s, timing_pair(a->timing_events, 0));
   if (e != hipSuccess) return fail(ASTR_ERR_HIP, "prefill kernel launch: %s", hipGetErrorString(e));
-  st = record_event(a->timing_events, 1, s);
-  if (st != ASTR_OK) return st;
   return ok();
 }
 

@@ -510,30 +510,27 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const D
 }
 
 template <int D, int G>
-hipError_t launch_split_t(const DecodeLaunch& p, hipStream_t s) {
-  if (p.off32)
-    hipLaunchKernelGGL((decode_split_kernel<D, G, true>), dim3(p.num_splits, p.num_kv_heads, 1), dim3(kThreads), 0, s, p);
-  else
-    hipLaunchKernelGGL((decode_split_kernel<D, G, false>), dim3(p.num_splits, p.num_kv_heads, 1), dim3(kThreads), 0, s, p);
-  return hipGetLastError();
+hipError_t launch_split_t(const DecodeLaunch& p, hipStream_t s, const Timing& t) {
+  const dim3 grid(p.num_splits, p.num_kv_heads, 1);
+  if (p.off32) return launch_kernel(decode_split_kernel<D, G, true>, grid, dim3(kThreads), s, t, p);
+  return launch_kernel(decode_split_kernel<D, G, false>, grid, dim3(kThreads), s, t, p);
 }
 
 template <int D, int G>
-hipError_t launch_combine_t(const DecodeLaunch& p, hipStream_t s) {
-  hipLaunchKernelGGL((decode_combine_kernel<D, G>), dim3(p.batch, p.num_kv_heads, 1), dim3(kCombineThreads), 0, s, p);
-  return hipGetLastError();
+hipError_t launch_combine_t(const DecodeLaunch& p, hipStream_t s, const Timing& t) {
+  return launch_kernel(decode_combine_kernel<D, G>, dim3(p.batch, p.num_kv_heads, 1), dim3(kCombineThreads), s, t, p);
 }
 
 #define ASTR_DECODE_CASES(FN)                       \
   switch (p.head_dim * 100 + p.group) {             \
-    case 6401: return FN<64, 1>(p, s);              \
-    case 6402: return FN<64, 2>(p, s);              \
-    case 6404: return FN<64, 4>(p, s);              \
-    case 6408: return FN<64, 8>(p, s);              \
-    case 12801: return FN<128, 1>(p, s);            \
-    case 12802: return FN<128, 2>(p, s);            \
-    case 12804: return FN<128, 4>(p, s);            \
-    case 12808: return FN<128, 8>(p, s);            \
+    case 6401: return FN<64, 1>(p, s, t);              \
+    case 6402: return FN<64, 2>(p, s, t);              \
+    case 6404: return FN<64, 4>(p, s, t);              \
+    case 6408: return FN<64, 8>(p, s, t);              \
+    case 12801: return FN<128, 1>(p, s, t);            \
+    case 12802: return FN<128, 2>(p, s, t);            \
+    case 12804: return FN<128, 4>(p, s, t);            \
+    case 12808: return FN<128, 8>(p, s, t);            \
     default: return hipErrorInvalidValue;           \
   }
 
@@ -543,8 +540,8 @@ bool decode_supported(int head_dim, int group) {
   return (head_dim == 64 || head_dim == 128) && (group == 1 || group == 2 || group == 4 || group == 8);
 }
 
-hipError_t launch_decode_split(const DecodeLaunch& p, hipStream_t s) { ASTR_DECODE_CASES(launch_split_t) }
+hipError_t launch_decode_split(const DecodeLaunch& p, hipStream_t s, const Timing& t) { ASTR_DECODE_CASES(launch_split_t) }
 
-hipError_t launch_decode_combine(const DecodeLaunch& p, hipStream_t s) { ASTR_DECODE_CASES(launch_combine_t) }
+hipError_t launch_decode_combine(const DecodeLaunch& p, hipStream_t s, const Timing& t) { ASTR_DECODE_CASES(launch_combine_t) }
 
 }  // namespace astr

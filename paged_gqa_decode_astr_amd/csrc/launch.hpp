@@ -2,6 +2,7 @@
 // Plain structs: every field is already validated by the ABI layer.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -48,10 +49,26 @@ struct PrefillLaunch {
   int32_t max_q_len;     // grid covers query positions [0, max_q_len)
 };
 
+// Optional events stamped by the dispatch itself at the kernel's start and
+// end (hipExtLaunchKernel), so their difference is the kernel's own duration.
+struct Timing {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
+template <typename Kernel, typename Args>
+hipError_t launch_kernel(Kernel kernel, dim3 grid, dim3 block, hipStream_t s, const Timing& t, const Args& args) {
+  if (t.start != nullptr || t.stop != nullptr)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, t.start, t.stop, 0, args);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, args);
+  return hipGetLastError();
+}
+
 // Each returns the launch status (hipGetLastError after the launch).
-hipError_t launch_decode_split(const DecodeLaunch& p, hipStream_t stream);
-hipError_t launch_decode_combine(const DecodeLaunch& p, hipStream_t stream);
-hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream);
+hipError_t launch_decode_split(const DecodeLaunch& p, hipStream_t stream, const Timing& t);
+hipError_t launch_decode_combine(const DecodeLaunch& p, hipStream_t stream, const Timing& t);
+hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream, const Timing& t);
 
 // Whether a (head_dim, group) pair has a compiled kernel.
 bool decode_supported(int head_dim, int group);

@@ -215,11 +215,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillLaunch p
 }
 
 template <int D, int G>
-hipError_t launch_t(const PrefillLaunch& p, hipStream_t s) {
+hipError_t launch_t(const PrefillLaunch& p, hipStream_t s, const Timing& t) {
   constexpr int BQ = kRows / G;
   const int qtiles = (p.max_q_len + BQ - 1) / BQ;
-  hipLaunchKernelGGL((prefill_kernel<D, G>), dim3(qtiles, p.num_kv_heads, p.batch), dim3(kThreads), 0, s, p);
-  return hipGetLastError();
+  return launch_kernel(prefill_kernel<D, G>, dim3(qtiles, p.num_kv_heads, p.batch), dim3(kThreads), s, t, p);
 }
 
 }  // namespace
@@ -228,16 +227,16 @@ bool prefill_supported(int head_dim, int group) {
   return (head_dim == 64 || head_dim == 128) && (group == 1 || group == 2 || group == 4 || group == 8);
 }
 
-hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t s) {
+hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t s, const Timing& t) {
   switch (p.head_dim * 100 + p.group) {
-    case 6401: return launch_t<64, 1>(p, s);
-    case 6402: return launch_t<64, 2>(p, s);
-    case 6404: return launch_t<64, 4>(p, s);
-    case 6408: return launch_t<64, 8>(p, s);
-    case 12801: return launch_t<128, 1>(p, s);
-    case 12802: return launch_t<128, 2>(p, s);
-    case 12804: return launch_t<128, 4>(p, s);
-    case 12808: return launch_t<128, 8>(p, s);
+    case 6401: return launch_t<64, 1>(p, s, t);
+    case 6402: return launch_t<64, 2>(p, s, t);
+    case 6404: return launch_t<64, 4>(p, s, t);
+    case 6408: return launch_t<64, 8>(p, s, t);
+    case 12801: return launch_t<128, 1>(p, s, t);
+    case 12802: return launch_t<128, 2>(p, s, t);
+    case 12804: return launch_t<128, 4>(p, s, t);
+    case 12808: return launch_t<128, 8>(p, s, t);
     default: return hipErrorInvalidValue;
   }
 }

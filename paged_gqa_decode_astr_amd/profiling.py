@@ -1,0 +1,276 @@
+"""rocprofv3 measurements of the decode kernels.
+
+Three subcommands:
+
+  workload  the program that is profiled: warm-up and timed decode calls over
+            rotating seeded input sets, then a plain copy kernel of known size
+            (y = -x over 1 GiB of fp32) used to calibrate the HBM counters.
+  pmc       runs `workload` under two rocprofv3 --pmc passes (FETCH_SIZE, then
+            WRITE_SIZE), scales the split kernel's per-dispatch counts by what
+            the same counters read for the copy kernel, and writes
+            profiles/decode_split_<config>_pmc.{json,md}.
+  trace     runs bench.py under rocprofv3 --kernel-trace --stats and writes
+            profiles/decode_<config>_kernel_trace.md.
+
+`pmc` and `trace` never touch the GPU themselves (rocprofv3 starts the
+profiled program as a child process).  Algorithmic byte counts live here too,
+so that bench.py and the summaries use one definition.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import shlex
+import statistics
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+PROFILES = os.path.join(ROOT, "profiles")
+# Files whose contents decide what the split kernel reads: a stored counter
+# summary is used only while they are unchanged.
+TRAFFIC_SOURCES = ("paged_gqa_decode_astr_amd/csrc/decode.hip", "paged_gqa_decode_astr_amd/csrc/api.cpp")
+COPY_ELEMS = 1 << 28          # fp32 elements of the calibration copy (1 GiB read + 1 GiB written)
+COPY_REPS = 4
+
+
+# ----------------------------------------------------------------------------- algorithmic bytes
+
+def decode_bytes(inp, with_lse=True):
+    """Algorithmic HBM bytes of one decode call, each byte counted once: K and V rows of every
+    (key, kv head), q and o, req_to_token entries, kv_indptr and lse."""
+    B, Hq, D = inp["q"].shape
+    Hkv = inp["num_kv_heads"]
+    N = int(inp["kv_indptr"][-1])
+    kv = N * Hkv * D * 2 * 2
+    qo = 2 * B * Hq * D * 2
+    idx = N * 4 + (B + 1) * 4
+    return kv + qo + idx + (B * Hq * 4 if with_lse else 0)
+
+
+def split_kernel_bytes(inp):
+    """Bytes the split kernel must read: K + V + q + req_to_token entries + kv_indptr."""
+    B, Hq, D = inp["q"].shape
+    Hkv = inp["num_kv_heads"]
+    N = int(inp["kv_indptr"][-1])
+    return N * Hkv * D * 2 * 2 + B * Hq * D * 2 + N * 4 + (B + 1) * 4
+
+
+def sources_digest():
+    return {p: hashlib.sha256(open(os.path.join(ROOT, p), "rb").read()).hexdigest() for p in TRAFFIC_SOURCES}
+
+
+def read_traffic(config):
+    """HBM bytes per split-kernel launch from the stored counter summary, or None when there is
+    none or the kernel sources changed since it was taken."""
+    path = os.path.join(PROFILES, f"decode_split_{config}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("sources") != sources_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------- profiled program
+
+def _workload(args):
+    import torch
+
+    from . import _lib, tensors
+    _lib.load_library()
+    sets = tensors.decode_sets(args.config, args.sets, "cuda", num_splits=args.num_splits)
+    torch.cuda.synchronize()
+    for k in range(args.warmup + args.calls):
+        tensors.decode_step(sets, k, num_splits=args.num_splits)
+    torch.cuda.synchronize()
+    x = torch.ones(COPY_ELEMS, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(COPY_REPS):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    print(f"[workload] {args.config}: {args.warmup}+{args.calls} decode calls over {args.sets} sets, "
+          f"{COPY_REPS} copies of {COPY_ELEMS * 4} bytes", flush=True)
+    return 0
+
+
+def _workload_cmd(args):
+    return [sys.executable, "-m", "paged_gqa_decode_astr_amd.profiling", "workload", "--config", args.config,
+            "--sets", str(args.sets), "--warmup", str(args.warmup), "--calls", str(args.calls),
+            "--num-splits", str(args.num_splits)]
+
+
+def _run_profiler(cmd, log_path, timeout_s):
+    """rocprofv3 as a child process (from /tmp, TMPDIR=/tmp); SIGKILL after timeout_s."""
+    env = dict(os.environ, TMPDIR="/tmp", PYTHONPATH=ROOT + os.pathsep + os.environ.get("PYTHONPATH", ""))
+    full = ["timeout", "-s", "KILL", str(timeout_s)] + cmd
+    print("[profile] " + " ".join(shlex.quote(c) for c in full), flush=True)
+    with open(log_path, "w") as log:
+        rc = subprocess.run(full, cwd="/tmp", env=env, stdout=log, stderr=subprocess.STDOUT).returncode
+    if rc != 0:
+        with open(log_path) as fh:
+            tail = fh.read()[-2000:]
+        raise SystemExit(f"profiler run failed (rc={rc}); log tail:\n{tail}")
+
+
+def _counter_rows(raw_dir):
+    files = glob.glob(os.path.join(raw_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {raw_dir}")
+    per = {}
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                key = int(r["Dispatch_Id"])
+                ent = per.setdefault(key, {"name": r["Kernel_Name"], "values": {}})
+                ent["values"][r["Counter_Name"]] = ent["values"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return [per[k] for k in sorted(per)]
+
+
+def _per_dispatch(rows, counter, match, last=None):
+    vals = [r["values"][counter] for r in rows if match in r["name"] and counter in r["values"]]
+    if last is not None:
+        vals = vals[-last:]
+    if not vals:
+        names = sorted({r["name"][:80] for r in rows})
+        raise SystemExit(f"no dispatch of a kernel matching {match!r} with {counter}; kernels seen: {names}")
+    return vals
+
+
+def _pmc(args):
+    from .workloads import make_inputs
+    raw = os.path.abspath(args.raw)
+    os.makedirs(raw, exist_ok=True)
+    wl = _workload_cmd(args)
+    measured = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        out = os.path.join(raw, counter)
+        cmd = ["rocprofv3", "--pmc", counter, "--output-format", "csv", "-d", out, "-o", "run", "--"] + wl
+        _run_profiler(cmd, os.path.join(raw, f"{counter}.log"), args.timeout)
+        rows = _counter_rows(out)
+        split = _per_dispatch(rows, counter, "decode_split_kernel", last=args.calls)
+        copy = _per_dispatch(rows, counter, "neg", last=COPY_REPS)
+        measured[counter] = {"split_kib": split, "copy_kib": copy}
+
+    copy_bytes = COPY_ELEMS * 4
+    f_read = copy_bytes / (statistics.median(measured["FETCH_SIZE"]["copy_kib"]) * 1024)
+    f_write = copy_bytes / (statistics.median(measured["WRITE_SIZE"]["copy_kib"]) * 1024)
+    fetch = statistics.mean(measured["FETCH_SIZE"]["split_kib"]) * 1024 * f_read
+    write = statistics.mean(measured["WRITE_SIZE"]["split_kib"]) * 1024 * f_write
+    # Dispatch i of the measured calls used set (warmup + i) mod sets.
+    per_set = [split_kernel_bytes(make_inputs(args.config, t)) for t in range(args.sets)]
+    algo = statistics.mean(per_set[(args.warmup + i) % args.sets] for i in range(args.calls))
+    pass_cmd = ("cd /tmp && TMPDIR=/tmp timeout -s KILL {t} rocprofv3 --pmc {c} --output-format csv -d <raw>/{c} "
+                "-o run -- " + " ".join(shlex.quote(c) for c in wl))
+    rec = {
+        "kernel": "decode_split_kernel",
+        "workload": args.config,
+        "command": "python3 -m paged_gqa_decode_astr_amd.profiling pmc " + " ".join(
+            f"--{k.replace('_', '-')} {v}" for k, v in [("config", args.config), ("sets", args.sets),
+                                                       ("warmup", args.warmup), ("calls", args.calls),
+                                                       ("num_splits", args.num_splits)]),
+        "passes": [pass_cmd.format(t=args.timeout, c=c) for c in ("FETCH_SIZE", "WRITE_SIZE")],
+        "sources": sources_digest(),
+        "dispatches": args.calls,
+        "split_fetch_kib_mean": statistics.mean(measured["FETCH_SIZE"]["split_kib"]),
+        "split_write_kib_mean": statistics.mean(measured["WRITE_SIZE"]["split_kib"]),
+        "copy_bytes_each_way": copy_bytes,
+        "copy_fetch_kib_median": statistics.median(measured["FETCH_SIZE"]["copy_kib"]),
+        "copy_write_kib_median": statistics.median(measured["WRITE_SIZE"]["copy_kib"]),
+        "read_scale": f_read,
+        "write_scale": f_write,
+        "hbm_read_bytes_per_launch": fetch,
+        "hbm_write_bytes_per_launch": write,
+        "hbm_bytes_per_launch": fetch + write,
+        "algorithmic_bytes_per_launch": algo,
+        "traffic_over_algorithmic": (fetch + write) / algo,
+    }
+    os.makedirs(PROFILES, exist_ok=True)
+    base = os.path.join(PROFILES, f"decode_split_{args.config}_pmc")
+    with open(base + ".json", "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    with open(base + ".md", "w") as fh:
+        fh.write(f"# decode_split_kernel HBM traffic, workload {args.config}\n\n")
+        fh.write(f"Command: `{rec['command']}`\n\nPasses (each its own rocprofv3 run):\n\n")
+        for c in rec["passes"]:
+            fh.write(f"- `{c}`\n")
+        fh.write("\n| quantity | value |\n|---|---|\n")
+        for k in ("dispatches", "split_fetch_kib_mean", "split_write_kib_mean", "copy_bytes_each_way",
+                  "copy_fetch_kib_median", "copy_write_kib_median", "read_scale", "write_scale",
+                  "hbm_read_bytes_per_launch", "hbm_write_bytes_per_launch", "hbm_bytes_per_launch",
+                  "algorithmic_bytes_per_launch", "traffic_over_algorithmic"):
+            v = rec[k]
+            fh.write(f"| {k} | {v:.6g} |\n" if isinstance(v, float) else f"| {k} | {v} |\n")
+        fh.write("\nCounters are FETCH_SIZE / WRITE_SIZE in KiB per dispatch, summed over instances; the scales "
+                 "make the copy kernel (y = -x over 1 GiB of fp32) read and write exactly its size.\n")
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def _trace(args, bench_args):
+    raw = os.path.abspath(args.raw)
+    os.makedirs(raw, exist_ok=True)
+    bench_cmd = [sys.executable, os.path.join(ROOT, "bench.py")] + bench_args
+    cmd = ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d", raw, "-o", "run", "--"] + bench_cmd
+    _run_profiler(cmd, os.path.join(raw, "trace.log"), args.timeout)
+    stats = glob.glob(os.path.join(raw, "**", "*kernel_stats.csv"), recursive=True)
+    if not stats:
+        raise SystemExit(f"no kernel_stats.csv under {raw}")
+    with open(stats[0]) as fh:
+        rows = list(csv.DictReader(fh))
+    bench = None
+    with open(os.path.join(raw, "trace.log")) as fh:
+        for line in fh:
+            if line.startswith("{") and '"metric"' in line:
+                bench = json.loads(line)
+    shown = " ".join(shlex.quote(c) for c in ["python3", "bench.py"] + bench_args)
+    path = os.path.join(PROFILES, f"decode_{args.config}_kernel_trace.md")
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(path, "w") as fh:
+        fh.write(f"# Kernel trace of the decode benchmark, workload {args.config}\n\n")
+        fh.write("Command: `cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats --output-format csv "
+                 f"-d <raw> -o run -- {shown}`\n\n")
+        fh.write("| kernel | calls | average (us) | min (us) | max (us) | share of GPU time (%) |\n|---|---|---|---|---|---|\n")
+        for r in rows[: args.top]:
+            fh.write(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |\n")
+        if bench is not None:
+            fh.write(f"\nbench.py under the profiler: whole call {bench['us_per_call']} us.  (Its dispatch-stamped "
+                     "event timings are not quoted here: the profiler's per-dispatch work lands inside them.)\n")
+    print(open(path).read(), flush=True)
+    return 0
+
+
+def main(argv=None):
+    argv = list(sys.argv[1:] if argv is None else argv)
+    bench_args = []
+    if "--" in argv:
+        i = argv.index("--")
+        argv, bench_args = argv[:i], argv[i + 1:]
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("mode", choices=["workload", "pmc", "trace"])
+    ap.add_argument("--config", default="decode_b32")
+    ap.add_argument("--sets", type=int, default=4)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--calls", type=int, default=40)
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--raw", default="gpurun_out/prof", help="directory for rocprofv3's raw output")
+    ap.add_argument("--timeout", type=int, default=240, help="seconds before a profiler run is killed")
+    ap.add_argument("--top", type=int, default=8, help="kernels listed in the trace summary")
+    args = ap.parse_args(argv)
+    if args.mode == "workload":
+        return _workload(args)
+    if args.mode == "pmc":
+        return _pmc(args)
+    return _trace(args, bench_args or ["--cpu-seconds", "0"])
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -67,3 +67,25 @@ def run_prefill(dev: dict, o=None, lse=None, max_q_len=0, stream=None, timing_ev
 
 def bf16_to_f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().to(torch.float64).cpu().numpy()
+
+
+def decode_sets(config: str, nsets: int, device="cuda", num_splits: int = 0):
+    """`nsets` independent seeded batches of a decode workload, resident on the device, each with its
+    own output, lse and workspace.  Rotating over them keeps each call's K/V out of the caches."""
+    from .workloads import make_inputs
+    sets = []
+    for t in range(nsets):
+        inp = make_inputs(config, t)
+        d = to_device(inp, device)
+        B, Hq, D = inp["q"].shape
+        d["o"] = torch.empty(B, Hq, D, dtype=torch.bfloat16, device=device)
+        d["lse"] = torch.empty(B, Hq, dtype=torch.float32, device=device)
+        d["ws"] = decode_workspace(B, Hq, D, device, max_splits=num_splits)
+        sets.append((inp, d))
+    return sets
+
+
+def decode_step(sets, k: int, num_splits: int = 0, timing_events=None):
+    """One decode call on set k mod len(sets)."""
+    _, d = sets[k % len(sets)]
+    run_decode(d, o=d["o"], lse=d["lse"], workspace=d["ws"], timing_events=timing_events, num_splits=num_splits)
