@@ -41,7 +41,7 @@
 // At the end of a piece the 4 wavefronts merge through LDS and one normalised
 // partial (o, m, l) per query head is written.
 #include "device_common.hpp"
-#include "launch.hpp"
+#include "kernel_launch.hpp"
 
 namespace astr {
 namespace {
@@ -410,24 +410,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   }
 }
 
-// One work group per (request, kv head): merges the pieces w_first..w_last
-// of the request for the G query heads of kv head g.  kGroups thread groups
-// take interleaved pieces; each thread folds its pieces into (M, den, num)
-// for its (head, d) outputs with an online log-sum-exp merge, kBatch pieces
-// at a time so their loads are in flight together; the groups then merge
-// through LDS.
+// One work group of D threads per (request, query head): thread d folds the
+// request's pieces w_first..w_last into (M, den, num) for output element d
+// with an online log-sum-exp merge, kBatch pieces at a time so that their
+// loads are in flight together, then writes O (bf16, round to nearest even)
+// and lse = M + ln(den).
 constexpr int kBatch = 8;
-constexpr int kGroups = 4;
-constexpr int kCombineThreads = kThreads * kGroups;
 
 template <int D, int G>
-__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const DecodeLaunch p) {
-  constexpr int kPer = (G * D + kThreads - 1) / kThreads;   // outputs per thread
-  __shared__ float s_part[kGroups - 1][3][kPer][kThreads];
+__global__ __launch_bounds__(D) void decode_combine_kernel(const DecodeLaunch p) {
   const int b = blockIdx.x;
-  const int g = blockIdx.y;
-  const int tid = threadIdx.x % kThreads;
-  const int grp = threadIdx.x / kThreads;
+  const int h = blockIdx.y;
+  const int d = threadIdx.x;
   const int64_t N = p.kv_indptr[p.batch];
   const int64_t x0 = p.kv_indptr[b];
   const int64_t x1 = (int64_t)p.kv_indptr[b + 1] - 1;
@@ -435,78 +429,38 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const D
   const int wf = (int)(((x0 + 1) * W + N - 1) / N - 1);
   const int wl = (int)(((x1 + 1) * W + N - 1) / N - 1);
   const int n = wl - wf + 1;
-  float Ms[kPer], dens[kPer], nums[kPer];
+  const int64_t base = (int64_t)h * p.num_partials + b + wf;
+  const float* ml = p.ml_part + base * 2;
+  const float* op = p.o_part + base * D + d;
+  float M = -INFINITY, den = 0.f, num = 0.f;
+  for (int i0 = 0; i0 < n; i0 += kBatch) {
+    float m[kBatch], l[kBatch], o[kBatch];
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int idx = tid + j * kThreads;
-    float M = -INFINITY, den = 0.f, num = 0.f;
-    if (idx < G * D) {
-      const int hh = idx / D, d = idx % D;
-      const int64_t base = (int64_t)(g * G + hh) * p.num_partials + b + wf;
-      const float* ml = p.ml_part + base * 2;
-      const float* op = p.o_part + base * D + d;
-      for (int i0 = grp; i0 < n; i0 += kBatch * kGroups) {
-        float m[kBatch], l[kBatch], o[kBatch];
-#pragma unroll
-        for (int i = 0; i < kBatch; ++i) {
-          const int pi = min(i0 + i * kGroups, n - 1);
-          m[i] = ml[2 * pi];
-          l[i] = ml[2 * pi + 1];
-          o[i] = op[(int64_t)pi * D];
-        }
-        float Mb = M;
-#pragma unroll
-        for (int i = 0; i < kBatch; ++i)
-          if (i0 + i * kGroups < n) Mb = fmaxf(Mb, m[i]);
-        const float sc = expf(M - Mb);   // M == -inf on the first batch: scales zeros
-        den *= sc;
-        num *= sc;
-#pragma unroll
-        for (int i = 0; i < kBatch; ++i) {
-          if (i0 + i * kGroups >= n) continue;
-          const float wgt = l[i] * expf(m[i] - Mb);
-          den += wgt;
-          num = fmaf(wgt, o[i], num);
-        }
-        M = Mb;
-      }
+    for (int i = 0; i < kBatch; ++i) {
+      const int pi = min(i0 + i, n - 1);
+      const float2 mlv = *reinterpret_cast<const float2*>(ml + 2 * pi);
+      m[i] = mlv.x;
+      l[i] = mlv.y;
+      o[i] = op[(int64_t)pi * D];
     }
-    Ms[j] = M;
-    dens[j] = den;
-    nums[j] = num;
-  }
-  if (grp > 0) {
+    float Mb = M;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      s_part[grp - 1][0][j][tid] = Ms[j];
-      s_part[grp - 1][1][j][tid] = dens[j];
-      s_part[grp - 1][2][j][tid] = nums[j];
+    for (int i = 0; i < kBatch; ++i)
+      if (i0 + i < n) Mb = fmaxf(Mb, m[i]);
+    const float sc = expf(M - Mb);
+    den *= sc;
+    num *= sc;
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      if (i0 + i >= n) continue;
+      const float wgt = l[i] * expf(m[i] - Mb);
+      den += wgt;
+      num = fmaf(wgt, o[i], num);
     }
+    M = Mb;
   }
-  __syncthreads();
-  if (grp > 0) return;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int idx = tid + j * kThreads;
-    if (idx >= G * D) break;
-    float M = Ms[j];
-#pragma unroll
-    for (int k = 0; k < kGroups - 1; ++k) M = fmaxf(M, s_part[k][0][j][tid]);
-    float den = dens[j] * expf(Ms[j] - M);   // group 0 always holds piece 0: Ms[j] is finite
-    float num = nums[j] * expf(Ms[j] - M);
-#pragma unroll
-    for (int k = 0; k < kGroups - 1; ++k) {
-      const float mk = s_part[k][0][j][tid];
-      if (mk == -INFINITY) continue;   // group had no piece
-      const float sc = expf(mk - M);
-      den = fmaf(s_part[k][1][j][tid], sc, den);
-      num = fmaf(s_part[k][2][j][tid], sc, num);
-    }
-    const int hh = idx / D, d = idx % D;
-    const int h = g * G + hh;
-    p.o[(int64_t)b * p.o_stride_tok + (int64_t)h * p.o_stride_head + d] = f32_to_bf16_rne(num / den);
-    if (p.lse != nullptr && d == 0) p.lse[(int64_t)b * p.lse_stride_tok + h] = M + logf(den);
-  }
+  p.o[(int64_t)b * p.o_stride_tok + (int64_t)h * p.o_stride_head + d] = f32_to_bf16_rne(num / den);
+  if (p.lse != nullptr && d == 0) p.lse[(int64_t)b * p.lse_stride_tok + h] = M + logf(den);
 }
 
 template <int D, int G>
@@ -518,7 +472,7 @@ hipError_t launch_split_t(const DecodeLaunch& p, hipStream_t s, const Timing& t)
 
 template <int D, int G>
 hipError_t launch_combine_t(const DecodeLaunch& p, hipStream_t s, const Timing& t) {
-  return launch_kernel(decode_combine_kernel<D, G>, dim3(p.batch, p.num_kv_heads, 1), dim3(kCombineThreads), s, t, p);
+  return launch_kernel(decode_combine_kernel<D, G>, dim3(p.batch, p.num_qo_heads, 1), dim3(D), s, t, p);
 }
 
 #define ASTR_DECODE_CASES(FN)                       \

@@ -2,7 +2,6 @@
 // Plain structs: every field is already validated by the ABI layer.
 #pragma once
 
-#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -55,15 +54,6 @@ struct Timing {
   hipEvent_t start = nullptr;
   hipEvent_t stop = nullptr;
 };
-
-template <typename Kernel, typename Args>
-hipError_t launch_kernel(Kernel kernel, dim3 grid, dim3 block, hipStream_t s, const Timing& t, const Args& args) {
-  if (t.start != nullptr || t.stop != nullptr)
-    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, t.start, t.stop, 0, args);
-  else
-    hipLaunchKernelGGL(kernel, grid, block, 0, s, args);
-  return hipGetLastError();
-}
 
 // Each returns the launch status (hipGetLastError after the launch).
 hipError_t launch_decode_split(const DecodeLaunch& p, hipStream_t stream, const Timing& t);

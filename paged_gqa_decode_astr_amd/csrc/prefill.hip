@@ -21,7 +21,7 @@
 //     32-key step permuted identically in both operands.
 // Output rows are normalised by the row sum of the same bf16-rounded weights.
 #include "device_common.hpp"
-#include "launch.hpp"
+#include "kernel_launch.hpp"
 
 namespace astr {
 namespace {
