@@ -127,11 +127,14 @@ int validate_common(const astr_paged_args* a, bool prefill, int64_t* total_keys)
   return ASTR_OK;
 }
 
-// Whether every byte offset of a pool row from its kv-head base,
-// slot * kv_stride_slot * 2 + head_dim * 2, stays below 2^32.
-bool pool_offsets_fit_32(const astr_paged_args* a) {
-  const int64_t last = (a->num_slots - 1) * a->kv_stride_slot * 2 + (int64_t)a->head_dim * 2;
-  return last < ((int64_t)1 << 32);
+// Bytes from a kv head's base to the end of that head's row in the last
+// slot: (num_slots - 1) * kv_stride_slot * 2 + head_dim * 2.  The decode
+// kernel takes 32-bit buffer offsets when this is at most kPoolRange32 (the
+// offsets above it are its out-of-range marker).
+constexpr int64_t kPoolRange32 = 0xFFFFF000;
+
+int64_t pool_range_bytes(const astr_paged_args* a) {
+  return (a->num_slots - 1) * a->kv_stride_slot * 2 + (int64_t)a->head_dim * 2;
 }
 
 // The caller's timing events i and i + 1 (either may be NULL) as the start
@@ -143,6 +146,24 @@ astr::Timing timing_pair(void* const* events, int i) {
     t.stop = static_cast<hipEvent_t>(events[i + 1]);
   }
   return t;
+}
+
+// Thread groups for the combine kernel: enough that no group folds more than
+// two batches of 8 pieces for the request with the most pieces (from the
+// host copy of kv_indptr; the result does not depend on this choice).
+int32_t combine_groups(const astr_paged_args* a, int64_t total_keys, int64_t wh) {
+  if (a->batch <= 0 || total_keys <= 0) return 1;
+  const int64_t W = wh < total_keys ? wh : total_keys;
+  const int32_t* kv = a->kv_indptr_host;
+  int64_t most = 1;
+  for (int32_t b = 0; b < a->batch; ++b) {
+    // Work groups holding the request's first and last keys (ceil((x + 1) W / N) - 1).
+    const int64_t wf = ceil_div(((int64_t)kv[b] + 1) * W, total_keys) - 1;
+    const int64_t wl = ceil_div((int64_t)kv[b + 1] * W, total_keys) - 1;
+    if (wl - wf + 1 > most) most = wl - wf + 1;
+  }
+  const int64_t g = ceil_div(most, 16);
+  return (int32_t)(g < 1 ? 1 : (g > 8 ? 8 : g));
 }
 
 int plan_decode_impl(const astr_paged_args* a, int64_t total_keys, int32_t num_cus, astr_decode_plan* out) {
@@ -244,9 +265,12 @@ int astr_paged_decode(const astr_paged_args* a, void* workspace, size_t workspac
   p.req_to_token = a->req_to_token;
   p.req_to_token_stride = a->req_to_token_stride;
   p.kv_indptr = a->kv_indptr;
-  p.off32 = pool_offsets_fit_32(a);
+  const int64_t range = pool_range_bytes(a);
+  p.off32 = range <= kPoolRange32;
+  p.pool_range = p.off32 ? (uint32_t)range : 0u;
   p.num_splits = plan.num_splits;
   p.num_partials = plan.num_partials;
+  p.combine_groups = combine_groups(a, total, plan.num_splits);
   p.o_part = static_cast<float*>(workspace);
   p.ml_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                        align256((int64_t)a->num_qo_heads * plan.num_partials * a->head_dim * 4));

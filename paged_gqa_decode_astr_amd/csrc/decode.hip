@@ -86,37 +86,49 @@ struct Tile {
   uint4 v[Shape<D>::kSteps];
 };
 
-// Slot id of key t0 + l % 16.  Keys past the piece end are clamped to its last
-// key, so every load is unconditional: a branch around a load would keep the
-// compiler from counting outstanding loads, and it would then wait for the
-// prefetched tile before computing the current one.
-__device__ __forceinline__ int load_id(const int32_t* row, int t0, int t_end, int lane) {
-  return row[min(t0 + (lane & 15), t_end - 1)];
-}
-
 // Pool rows are addressed from a per-kv-head base (wavefront-uniform, so it
-// lives in scalar registers) plus a per-lane byte offset.  When every offset
-// fits in 32 bits (pools up to 4 GiB per kv-head stride range) the offset is
-// computed in 32-bit arithmetic and the loads use the scalar-base addressing
-// mode; larger pools take 64-bit offsets.
-template <bool OFF32>
-__device__ __forceinline__ uint4 load_row16(const char* base, int slot, int64_t row_bytes, int extra) {
-  if constexpr (OFF32) {
-    const uint32_t off = (uint32_t)slot * (uint32_t)row_bytes + (uint32_t)extra;
-    return *reinterpret_cast<const uint4*>(base + off);
-  } else {
-    return *reinterpret_cast<const uint4*>(base + (int64_t)slot * row_bytes + extra);
-  }
-}
+// lives in scalar registers) plus a per-lane byte offset.
+//
+// When every row of the head's range lies within kPoolRange32 bytes of the
+// base (OFF32), the loads are raw buffer loads over a resource covering
+// exactly that range, with 32-bit offsets.  A key past the end of its piece
+// (the tail of the last tile, pad tiles, tiles beyond the work group's last
+// piece) gets the offset kOob, which the range check turns into zeros with no
+// memory access.  Every load is still issued unconditionally: a branch around
+// a load would keep the compiler from counting outstanding loads, and it would
+// then wait for the prefetched tile before computing the current one.
+//
+// Larger pools take 64-bit global addresses; there keys past the piece end
+// re-read the piece's last key (the data is never used).
+constexpr uint32_t kOob = 0xFFFFF000u;
+constexpr int64_t kPoolRange32 = kOob;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+struct PoolView {
+  __amdgpu_buffer_rsrc_t k_rsrc, v_rsrc;   // OFF32: buffer resources over the head's rows
+  const char* kbase;                        // otherwise: global base pointers of the head
+  const char* vbase;
+  int64_t row_bytes;
+};
 
 template <int D, bool OFF32>
-__device__ __forceinline__ void load_tile(Tile<D>& t, const char* kbase, const char* vbase, int64_t row_bytes, int id,
-                                          int lane) {
+__device__ __forceinline__ void load_tile(Tile<D>& t, const PoolView& pv, int id, int lane) {
   const int kb = lane >> 4;
+  if constexpr (OFF32) {
+    const uint32_t base = id >= 0 ? (uint32_t)id * (uint32_t)pv.row_bytes + 16u * kb : kOob;
 #pragma unroll
-  for (int s = 0; s < Shape<D>::kSteps; ++s) {
-    t.k[s] = load_row16<OFF32>(kbase, id, row_bytes, 16 * kb + 64 * s);
-    t.v[s] = load_row16<OFF32>(vbase, id, row_bytes, 16 * kb + 64 * s);
+    for (int s = 0; s < Shape<D>::kSteps; ++s) {
+      t.k[s] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(pv.k_rsrc, base + 64 * s, 0, 0));
+      t.v[s] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(pv.v_rsrc, base + 64 * s, 0, 0));
+    }
+  } else {
+    const int64_t base = (int64_t)id * pv.row_bytes + 16 * kb;
+#pragma unroll
+    for (int s = 0; s < Shape<D>::kSteps; ++s) {
+      t.k[s] = *reinterpret_cast<const uint4*>(pv.kbase + base + 64 * s);
+      t.v[s] = *reinterpret_cast<const uint4*>(pv.vbase + base + 64 * s);
+    }
   }
 }
 
@@ -191,9 +203,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   const int kb = lane >> 4;
   const int hcol = l16 % G;     // query head of this lane's S^T / O^T column
   const float qscale = p.sm_scale * kLog2e;
-  const char* kbase = reinterpret_cast<const char*>(p.k_pool + (int64_t)g * p.kv_stride_head);
-  const char* vbase = reinterpret_cast<const char*>(p.v_pool + (int64_t)g * p.kv_stride_head);
-  const int64_t row_bytes = p.kv_stride_slot * 2;
+  PoolView pv;
+  pv.kbase = reinterpret_cast<const char*>(p.k_pool + (int64_t)g * p.kv_stride_head);
+  pv.vbase = reinterpret_cast<const char*>(p.v_pool + (int64_t)g * p.kv_stride_head);
+  pv.row_bytes = p.kv_stride_slot * 2;
+  if constexpr (OFF32) {
+    pv.k_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(pv.kbase), (short)0, (int)p.pool_range, 0x00020000);
+    pv.v_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(pv.vbase), (short)0, (int)p.pool_range, 0x00020000);
+  }
 
   // kv_indptr[0 .. min(B, kKvStage - 1)] -> LDS in one round trip.
   int kv_base = 0;
@@ -238,15 +255,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     pt.n = n;
     bnext = pt.b0 + n;
 
-    // Slot id of the tile at cursor cu for this lane's key (a past-the-end
-    // cursor re-reads the last key of the last piece; its data is never used).
+    // Slot id of this lane's key in the tile at cursor cu; -1 (OFF32) or the
+    // piece's last key (64-bit path) for a key past the piece end, and for
+    // every key of a past-the-end cursor.  The id itself is always read from
+    // a valid req_to_token entry.
     auto id_at = [&](const Cursor& cu) -> int {
       const int j = min(cu.j, pt.n - 1);
       const int t_end = pt.t_end(j);
-      const int t0 = cu.j < pt.n ? cu.t : t_end - 1;
+      const int t = (cu.j < pt.n ? cu.t : t_end) + l16;
       const int32_t* row = p.req_to_token + (p.req_to_token_stride > 0 ? (int64_t)(pt.b0 + j) * p.req_to_token_stride
                                                                         : (int64_t)pt.kv[j]);
-      return load_id(row, t0, t_end, lane);
+      const int id = row[min(t, t_end - 1)];
+      if constexpr (OFF32) return t < t_end ? id : -1;
+      return id;
     };
     // q rows of piece j's request: 16 bytes per thread for the first G*D/8 threads.
     constexpr int kQThreads = G * D / 8;
@@ -281,9 +302,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     int iA = id_at(c0);
     int iB = id_at(c1);
     Tile<D> A, Bt;
-    load_tile<D, OFF32>(A, kbase, vbase, row_bytes, iA, lane);
+    load_tile<D, OFF32>(A, pv, iA, lane);
     iA = id_at(c2);
-    load_tile<D, OFF32>(Bt, kbase, vbase, row_bytes, iB, lane);
+    load_tile<D, OFF32>(Bt, pv, iB, lane);
     q_store(0, q_first);
     __syncthreads();
 
@@ -345,7 +366,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     auto step = [&](Tile<D>& X, int& iX, int& iY) {
       compute(X);
       iY = id_at(c3);
-      load_tile<D, OFF32>(X, kbase, vbase, row_bytes, iX, lane);
+      load_tile<D, OFF32>(X, pv, iX, lane);
       c0 = c1;
       c1 = c2;
       c2 = c3;
@@ -410,18 +431,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   }
 }
 
-// One work group of D threads per (request, query head): thread d folds the
-// request's pieces w_first..w_last into (M, den, num) for output element d
-// with an online log-sum-exp merge, kBatch pieces at a time so that their
-// loads are in flight together, then writes O (bf16, round to nearest even)
-// and lse = M + ln(den).
+// One work group per (request, query head) with kCombineGroups groups of D
+// threads (the host picks the group count from the longest request's piece
+// count; any count gives the same result up to rounding order).  Thread d of
+// group r folds pieces r, r + groups, ... of the request, w_first..w_last,
+// into (M, den, num) for output element d with an online log-sum-exp merge,
+// kBatch pieces at a time so that their loads are in flight together.  The
+// groups then merge through LDS in group order, and group 0 writes O (bf16,
+// round to nearest even) and lse = M + ln(den).
 constexpr int kBatch = 8;
+constexpr int kMaxCombineGroups = 8;
 
 template <int D, int G>
-__global__ __launch_bounds__(D) void decode_combine_kernel(const DecodeLaunch p) {
+__global__ __launch_bounds__(D * kMaxCombineGroups) void decode_combine_kernel(const DecodeLaunch p) {
+  __shared__ float s_part[kMaxCombineGroups - 1][3][D];
   const int b = blockIdx.x;
   const int h = blockIdx.y;
-  const int d = threadIdx.x;
+  const int d = threadIdx.x % D;
+  const int grp = threadIdx.x / D;
+  const int ngrp = blockDim.x / D;
   const int64_t N = p.kv_indptr[p.batch];
   const int64_t x0 = p.kv_indptr[b];
   const int64_t x1 = (int64_t)p.kv_indptr[b + 1] - 1;
@@ -433,11 +461,11 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const DecodeLaunch p)
   const float* ml = p.ml_part + base * 2;
   const float* op = p.o_part + base * D + d;
   float M = -INFINITY, den = 0.f, num = 0.f;
-  for (int i0 = 0; i0 < n; i0 += kBatch) {
+  for (int i0 = grp; i0 < n; i0 += kBatch * ngrp) {
     float m[kBatch], l[kBatch], o[kBatch];
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
-      const int pi = min(i0 + i, n - 1);
+      const int pi = min(i0 + i * ngrp, n - 1);
       const float2 mlv = *reinterpret_cast<const float2*>(ml + 2 * pi);
       m[i] = mlv.x;
       l[i] = mlv.y;
@@ -446,18 +474,36 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const DecodeLaunch p)
     float Mb = M;
 #pragma unroll
     for (int i = 0; i < kBatch; ++i)
-      if (i0 + i < n) Mb = fmaxf(Mb, m[i]);
-    const float sc = expf(M - Mb);
+      if (i0 + i * ngrp < n) Mb = fmaxf(Mb, m[i]);
+    const float sc = expf(M - Mb);   // M == -inf on the first batch: scales zeros
     den *= sc;
     num *= sc;
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
-      if (i0 + i >= n) continue;
+      if (i0 + i * ngrp >= n) continue;
       const float wgt = l[i] * expf(m[i] - Mb);
       den += wgt;
       num = fmaf(wgt, o[i], num);
     }
     M = Mb;
+  }
+  if (ngrp > 1) {
+    if (grp > 0) {
+      s_part[grp - 1][0][d] = M;
+      s_part[grp - 1][1][d] = den;
+      s_part[grp - 1][2][d] = num;
+    }
+    __syncthreads();
+    if (grp > 0) return;
+    for (int k = 0; k < ngrp - 1; ++k) {
+      const float mk = s_part[k][0][d];
+      if (mk == -INFINITY) continue;   // group had no piece
+      const float Mn = fmaxf(M, mk);
+      const float a = expf(M - Mn), c = expf(mk - Mn);   // group 0 always holds piece 0: M is finite
+      den = den * a + s_part[k][1][d] * c;
+      num = num * a + s_part[k][2][d] * c;
+      M = Mn;
+    }
   }
   p.o[(int64_t)b * p.o_stride_tok + (int64_t)h * p.o_stride_head + d] = f32_to_bf16_rne(num / den);
   if (p.lse != nullptr && d == 0) p.lse[(int64_t)b * p.lse_stride_tok + h] = M + logf(den);
@@ -472,7 +518,7 @@ hipError_t launch_split_t(const DecodeLaunch& p, hipStream_t s, const Timing& t)
 
 template <int D, int G>
 hipError_t launch_combine_t(const DecodeLaunch& p, hipStream_t s, const Timing& t) {
-  return launch_kernel(decode_combine_kernel<D, G>, dim3(p.batch, p.num_qo_heads, 1), dim3(D), s, t, p);
+  return launch_kernel(decode_combine_kernel<D, G>, dim3(p.batch, p.num_qo_heads, 1), dim3(D * p.combine_groups), s, t, p);
 }
 
 #define ASTR_DECODE_CASES(FN)                       \

@@ -22,9 +22,11 @@ struct DecodeLaunch {
   const int32_t* req_to_token;
   int64_t req_to_token_stride;
   const int32_t* kv_indptr;
-  bool off32;            // every pool row offset from a kv-head base fits in 32 bits
+  bool off32;            // every pool row of a kv head lies within pool_range bytes of its base
+  uint32_t pool_range;   // off32: (num_slots - 1) * kv_stride_slot * 2 + head_dim * 2
   int32_t num_splits;    // Wh: work groups per kv head (grid.x)
   int32_t num_partials;  // P = Wh + B - 1 slots per query head
+  int32_t combine_groups;  // thread groups of the combine kernel (1..8)
   float* o_part;         // [Hq][P][D]
   float* ml_part;        // [Hq][P][2]
 };
