@@ -1,4 +1,4 @@
-// Ragged paged GQA prefill for gfx950 with bf16 MFMA (v_mfma_f32_16x16x32_bf16).
+// Ragged paged GQA prefill for gfx950 on the matrix cores.
 //
 // Method (AstrAI commit-list pages): [attention.py @c9ceca1], the commit that
 // batches the torch path: query row i of request b sits at absolute position
@@ -11,15 +11,26 @@
 // Work group = (query tile, kv head g, request b), 4 wavefronts.  The G query
 // heads that share kv head g are stacked with the positions into 128 rows
 // (row R = position * G + head), so each K/V tile staged in LDS serves all
-// of them.  Per 64-key tile:
-//   * K rows are staged row-major and V rows transposed (V^T[d][t]) in LDS;
-//   * each wavefront computes S^T = K Q^T for its 32 rows (A = K from LDS,
-//     B = Q^T held in registers), which leaves every lane with 16 logits of one
-//     row, so the row max / sum need only two cross-lane steps;
-//   * P^T is rounded to bf16 and fed straight back as the B operand of
-//     O^T += V^T P^T (A = V^T read from LDS), with the key order inside each
-//     32-key step permuted identically in both operands.
-// Output rows are normalised by the row sum of the same bf16-rounded weights.
+// of them; wavefront w owns rows 32 w .. 32 w + 31 as two 16-row blocks.
+// Per 64-key tile:
+//   * K and V rows are gathered through req_to_token into registers one tile
+//     ahead (slot ids one more tile ahead) and stored row-major into one of two
+//     LDS buffers, so a single barrier per tile separates producers and
+//     consumers;
+//   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (A = K rows from LDS, B = Q^T
+//     held in registers): lane l gets the logits of keys 4*(l/16)..+3 of each
+//     16-key block for row l % 16, so a row's max needs two cross-lane steps;
+//   * softmax in base 2 against a lazily raised per-row reference (the
+//     accumulators are rescaled only when a logit exceeds it by more than
+//     kTau), weights rounded to bf16; the row sum adds the rounded weights, so
+//     the output is an exact convex combination of the bf16-weighted rows;
+//   * O^T += V^T P^T on v_mfma_f32_16x16x32_bf16: P^T is already in the
+//     B-operand layout (k = 8*(l/16) + e covers keys 4*(l/16) + e of two
+//     adjacent 16-key blocks), and V^T is read from the row-major V tile with
+//     two transposing LDS reads (ds_read_b64_tr_b16) that follow the same key
+//     order.
+// Output rows are normalised by the row sum and written as bf16 (round to
+// nearest even); lse = reference + log2(sum), returned in natural-log units.
 #include "device_common.hpp"
 #include "kernel_launch.hpp"
 
@@ -27,30 +38,41 @@ namespace astr {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 
 constexpr int kThreads = 256;
-constexpr int kRows = 128;  // (position, head) rows per work group
-constexpr int KT = 64;      // keys per tile
+constexpr int kRows = 128;       // (position, head) rows per work group
+constexpr int KT = 64;           // keys per tile
+constexpr float kTau = 8.0f;     // log2 headroom before the accumulators are rescaled
 
 __device__ __forceinline__ uint4 load16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+__device__ __forceinline__ f32x4 mfma32k(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+template <int D>
+struct PShape {
+  static constexpr int kSteps = D / 32;                        // k-steps of S^T = K Q^T
+  static constexpr int kDBlocks = D / 16;                      // 16-wide d blocks of O^T
+  static constexpr int kKRow = D + 8;                          // LDS row stride of the K tile (elements)
+  static constexpr int kVRow = D + 16;                         // LDS row stride of the V tile (elements)
+  static constexpr int kThreadsPerKey = kThreads / KT;         // 4 gather threads per key
+  static constexpr int kLoads = D / 8 / kThreadsPerKey;        // 16-byte K (and V) loads per thread per tile
+};
+
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillLaunch p) {
-  constexpr int BQ = kRows / G;     // query positions per work group
-  constexpr int KSTR = D + 8;       // LDS row stride of K (elements)
-  constexpr int VSTR = KT + 8;      // LDS row stride of V^T (elements)
-  constexpr int DSTEPS = D / 32;    // k-steps of S^T = K Q^T
-  constexpr int DBLK = D / 16;      // 16-wide d blocks of O^T
-  constexpr int CPR = D / 8;        // 16-byte chunks per head row
-  constexpr int RPP = kThreads / CPR;
-  constexpr int PASSES = KT / RPP;
-  __shared__ __align__(16) uint16_t sK[KT * KSTR];
-  __shared__ __align__(16) uint16_t sVt[D * VSTR];
+  using S = PShape<D>;
+  constexpr int BQ = kRows / G;   // query positions per work group
+  constexpr int NS = S::kSteps;
+  constexpr int NB = S::kDBlocks;
+  constexpr int NL = S::kLoads;
+  __shared__ __align__(16) uint16_t sK[2][KT * S::kKRow];
+  __shared__ __align__(16) uint16_t sV[2][KT * S::kVRow];
 
   const int qt = blockIdx.x;
   const int g = blockIdx.y;
@@ -61,19 +83,49 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillLaunch p
   if (p0 >= qb) return;  // uniform over the work group
   const int kv0 = p.kv_indptr[b];
   const int L = p.kv_indptr[b + 1] - kv0;
-  const int cofs = L - qb;             // absolute position of query row 0
-  const int npos = min(BQ, qb - p0);   // valid positions in this tile
-  const int kv_end = cofs + p0 + npos; // keys [0, kv_end) are visible to some row
+  const int cofs = L - qb;              // absolute position of query row 0
+  const int npos = min(BQ, qb - p0);    // valid positions in this tile
+  const int kv_end = cofs + p0 + npos;  // keys [0, kv_end) are visible to some row
+  const int ntiles = (kv_end + KT - 1) / KT;
   const int32_t* ids = p.req_to_token + (p.req_to_token_stride > 0 ? (int64_t)b * p.req_to_token_stride : (int64_t)kv0);
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wv = tid / kWave;
+  const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int l16 = lane & 15;
   const int kb = lane >> 4;
 
-  // B operand of S^T = K Q^T: lane (r + 16 kb) holds Q[row r][32 ks + 8 kb .. +7].
-  bf16x8 qop[2][DSTEPS];
+  // Gather role: thread t loads NL 16-byte chunks of key t / 4 (quarter t % 4
+  // of the head row).  Keys past kv_end re-read key kv_end - 1 (finite data;
+  // every row masks them).
+  const int gkey = tid / S::kThreadsPerKey;
+  const int gcol = (tid % S::kThreadsPerKey) * (NL * 8);
+  const int64_t head_off = (int64_t)g * p.kv_stride_head + gcol;
+  auto load_id = [&](int t0) -> int { return ids[min(t0 + gkey, kv_end - 1)]; };
+  uint4 kreg[NL], vreg[NL];
+  auto gather = [&](int id) {
+    const int64_t off = (int64_t)id * p.kv_stride_slot + head_off;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      kreg[i] = load16(p.k_pool + off + 8 * i);
+      vreg[i] = load16(p.v_pool + off + 8 * i);
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      *reinterpret_cast<uint4*>(&sK[buf][gkey * S::kKRow + gcol + 8 * i]) = kreg[i];
+      *reinterpret_cast<uint4*>(&sV[buf][gkey * S::kVRow + gcol + 8 * i]) = vreg[i];
+    }
+  };
+
+  // Tile 0 in flight, tile 1's slot ids behind it.
+  int id_next = load_id(0);
+  gather(id_next);
+  id_next = load_id(KT);
+
+  // B operand of S^T = K Q^T: lane (r + 16 kb) holds Q[row r][32 ks + 8 kb .. +7] of each row block.
+  bf16x8 qop[2][NS];
   int lim[2];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
@@ -83,117 +135,113 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillLaunch p
     lim[rb] = cofs + p0 + posl;  // last key this row may see
     const bool ok = posl < npos;
 #pragma unroll
-    for (int ks = 0; ks < DSTEPS; ++ks) {
+    for (int ks = 0; ks < NS; ++ks) {
       uint4 v = make_uint4(0, 0, 0, 0);
       if (ok) v = load16(p.q + (int64_t)(q0 + p0 + posl) * p.q_stride_tok + (int64_t)head * p.q_stride_head + 32 * ks + 8 * kb);
       qop[rb][ks] = __builtin_bit_cast(bf16x8, v);
     }
   }
   const float qk_scale = p.sm_scale * kLog2e;
-  f32x4 acc[2][DBLK];
-  float m[2], lsum[2];
+  const int lim_min = cofs + p0;   // smallest row limit of the work group
+  f32x4 acc[2][NB];
+  float mref[2], lsum[2];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
-    m[rb] = -INFINITY;
+    mref[rb] = -INFINITY;
     lsum[rb] = 0.f;
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db) acc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int db = 0; db < NB; ++db) acc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const int tl0 = tid / CPR;
-  const int ch = tid % CPR;
-  const int64_t head_off = (int64_t)g * p.kv_stride_head + ch * 8;
+  stash(0);
+  __syncthreads();
 
-  for (int t0 = 0; t0 < kv_end; t0 += KT) {
-    uint4 kreg[PASSES], vreg[PASSES];
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    const int t0 = it * KT;
+    const bool more = it + 1 < ntiles;   // uniform
+    if (more) {
+      gather(id_next);
+      id_next = load_id(t0 + 2 * KT);
+    }
+    const uint16_t* kt = sK[buf];
+    const uint16_t* vt = sV[buf];
+
+    // S^T blocks: st[rb][tb][q] = S^T[t0 + 16 tb + 4 kb + q][row 16 rb + l16].
+    f32x4 st[2][4];
 #pragma unroll
-    for (int i = 0; i < PASSES; ++i) {
-      const int t = t0 + tl0 + RPP * i;
-      kreg[i] = make_uint4(0, 0, 0, 0);
-      vreg[i] = make_uint4(0, 0, 0, 0);
-      if (t < kv_end) {
-        const int64_t off = (int64_t)ids[t] * p.kv_stride_slot + head_off;
-        kreg[i] = load16(p.k_pool + off);
-        vreg[i] = load16(p.v_pool + off);
+    for (int tb = 0; tb < 4; ++tb) {
+      st[0][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      st[1][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < NS; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kt[(16 * tb + l16) * S::kKRow + 32 * ks + 8 * kb]);
+        st[0][tb] = mfma32k(a, qop[0][ks], st[0][tb]);
+        st[1][tb] = mfma32k(a, qop[1][ks], st[1][tb]);
       }
     }
-    __syncthreads();  // the previous tile's LDS reads are complete
-#pragma unroll
-    for (int i = 0; i < PASSES; ++i) {
-      const int tl = tl0 + RPP * i;
-      *reinterpret_cast<uint4*>(&sK[tl * KSTR + ch * 8]) = kreg[i];
-      const uint32_t w4[4] = {vreg[i].x, vreg[i].y, vreg[i].z, vreg[i].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sVt[(ch * 8 + 2 * e) * VSTR + tl] = (uint16_t)(w4[e] & 0xffffu);
-        sVt[(ch * 8 + 2 * e + 1) * VSTR + tl] = (uint16_t)(w4[e] >> 16);
-      }
-    }
-    __syncthreads();
 
-    const bool need_mask = (t0 + KT - 1) > (cofs + p0);
+    const bool need_mask = t0 + KT - 1 > lim_min;   // uniform
+    bf16x8 pop[2][2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      // S^T blocks: st[tb][q] = S^T[t0 + 16 tb + 4 kb + q][row 16 rb + l16]
-      f32x4 st[4];
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        st[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < DSTEPS; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sK[(16 * tb + l16) * KSTR + 32 * ks + 8 * kb]);
-          st[tb] = mfma16(a, qop[rb][ks], st[tb]);
-        }
-      }
       float sv[4][4];
       float tmax = -INFINITY;
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          float s = st[tb][q] * qk_scale;
-          if (need_mask && (t0 + 16 * tb + 4 * kb + q) > lim[rb]) s = -INFINITY;
+          float s = st[rb][tb][q] * qk_scale;
+          if (need_mask && t0 + 16 * tb + 4 * kb + q > lim[rb]) s = -INFINITY;
           sv[tb][q] = s;
           tmax = fmaxf(tmax, s);
         }
       tmax = xor_max<16, kWave>(tmax);
-      const float mnew = fmaxf(m[rb], tmax);
-      const float alpha = exp2f(m[rb] - mnew);
-      m[rb] = mnew;
-      lsum[rb] *= alpha;
+      const bool raise = tmax > mref[rb] + kTau;
+      if (__builtin_amdgcn_ballot_w64(raise) != 0) {   // uniform over the wavefront
+        const float mnew = fmaxf(mref[rb], tmax);
+        const float alpha = exp2f(mref[rb] - mnew);     // mref == -inf on the first tile: scales zeros
+        mref[rb] = mnew;
+        lsum[rb] *= alpha;
 #pragma unroll
-      for (int db = 0; db < DBLK; ++db) acc[rb][db] *= alpha;
-
-      uint32_t pk[4][2];
+        for (int db = 0; db < NB; ++db) acc[rb][db] *= alpha;
+      }
       float psum = 0.f;
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
+      for (int k2 = 0; k2 < 2; ++k2) {
+        bf16x8 v;
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const uint16_t lo = f32_to_bf16_rne(exp2f(sv[tb][2 * h2] - mnew));
-          const uint16_t hi = f32_to_bf16_rne(exp2f(sv[tb][2 * h2 + 1] - mnew));
-          psum += __uint_as_float((uint32_t)lo << 16) + __uint_as_float((uint32_t)hi << 16);
-          pk[tb][h2] = (uint32_t)lo | ((uint32_t)hi << 16);
+        for (int e = 0; e < 8; ++e) {
+          const __bf16 w = (__bf16)__builtin_amdgcn_exp2f(sv[2 * k2 + e / 4][e % 4] - mref[rb]);
+          psum += (float)w;
+          v[e] = w;
         }
+        pop[rb][k2] = v;
+      }
       lsum[rb] += psum;
+    }
 
+    // O^T += V^T P^T: A = V^T[16 db + l16][keys], keys in the same order as P^T's k slots.
+#pragma unroll
+    for (int db = 0; db < NB; ++db) {
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
-        // k-slot 8 kb + e holds key 32 k2 + 4 kb + e (e < 4) or 32 k2 + 16 + 4 kb + (e - 4).
-        const bf16x8 bop = __builtin_bit_cast(bf16x8, make_uint4(pk[2 * k2][0], pk[2 * k2][1], pk[2 * k2 + 1][0], pk[2 * k2 + 1][1]));
-#pragma unroll
-        for (int db = 0; db < DBLK; ++db) {
-          const uint16_t* vrow = &sVt[(16 * db + l16) * VSTR + 32 * k2 + 4 * kb];
-          const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
-          const bf16x8 aop = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-          acc[rb][db] = mfma16(aop, bop, acc[rb][db]);
-        }
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(vt + (32 * k2 + 4 * kb + (l16 >> 2)) * S::kVRow + 16 * db + 4 * (l16 & 3)));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(vt + (32 * k2 + 16 + 4 * kb + (l16 >> 2)) * S::kVRow + 16 * db + 4 * (l16 & 3)));
+        const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const bf16x8 aop = __builtin_bit_cast(bf16x8, both);
+        acc[0][db] = mfma32k(aop, pop[0][k2], acc[0][db]);
+        acc[1][db] = mfma32k(aop, pop[1][k2], acc[1][db]);
       }
     }
+
+    if (more) stash(buf ^ 1);   // that buffer was last read before the previous barrier
+    __syncthreads();
   }
 
-  // acc[rb][db][q] = O^T[d = 16 db + 4 kb + q][row 16 rb + l16] (unnormalised)
+  // acc[rb][db][q] = O^T[d = 16 db + 4 kb + q][row 16 rb + l16], relative to mref.
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     const float ltot = xor_sum<16, kWave>(lsum[rb]);
@@ -205,12 +253,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillLaunch p
     const float inv = 1.f / ltot;
     uint16_t* orow = p.o + (int64_t)row * p.o_stride_tok + (int64_t)head * p.o_stride_head;
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db) {
+    for (int db = 0; db < NB; ++db) {
       const uint32_t w0 = (uint32_t)f32_to_bf16_rne(acc[rb][db][0] * inv) | ((uint32_t)f32_to_bf16_rne(acc[rb][db][1] * inv) << 16);
       const uint32_t w1 = (uint32_t)f32_to_bf16_rne(acc[rb][db][2] * inv) | ((uint32_t)f32_to_bf16_rne(acc[rb][db][3] * inv) << 16);
       *reinterpret_cast<uint2*>(orow + 16 * db + 4 * kb) = make_uint2(w0, w1);
     }
-    if (p.lse != nullptr && kb == 0) p.lse[(int64_t)row * p.lse_stride_tok + head] = (m[rb] + log2f(ltot)) * kLn2;
+    if (p.lse != nullptr && kb == 0) p.lse[(int64_t)row * p.lse_stride_tok + head] = (mref[rb] + log2f(ltot)) * kLn2;
   }
 }
 
