@@ -81,7 +81,7 @@ typedef struct astr_paged_args {
   int32_t num_qo_heads;   /* Hq >= 1 */
   int32_t num_kv_heads;   /* Hkv >= 1, Hq % Hkv == 0, Hq / Hkv in {1, 2, 4, 8} */
   int32_t head_dim;       /* D in {64, 128} */
-  float sm_scale;         /* logit scale, e.g. 1/sqrt(D) */
+  float sm_scale;         /* logit scale, finite and > 0, e.g. 1/sqrt(D) */
 
   /* Queries, bf16.  Decode: row b is request b's query.  Prefill: rows in flat
    * qo_indptr order (row qo_indptr[b] + i is request b's i-th new token).

@@ -88,8 +88,8 @@ int validate_common(const astr_paged_args* a, bool prefill, int64_t* total_keys)
   if (!supported)
     return fail(ASTR_ERR_UNSUPPORTED, "no kernel for head_dim=%d and group size %d (head_dim in {64,128}, group in {1,2,4,8})",
                 a->head_dim, group);
-  if (!(a->sm_scale == a->sm_scale) || a->sm_scale == __builtin_inff() || a->sm_scale == -__builtin_inff())
-    return fail(ASTR_ERR_INVALID_ARG, "sm_scale must be finite");
+  if (!(a->sm_scale > 0.f) || a->sm_scale == __builtin_inff())
+    return fail(ASTR_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
   *total_keys = 0;
   if (a->batch == 0) return ASTR_OK;
 

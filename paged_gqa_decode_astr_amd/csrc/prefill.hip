@@ -8,10 +8,11 @@
 // prefill kernel tiles over queries and uses matrix instructions for QK^T and
 // PV; query head h reads kv head h / G.
 //
-// Work group = (query tile, kv head g, request b), 4 wavefronts.  The G query
-// heads that share kv head g are stacked with the positions into 128 rows
-// (row R = position * G + head), so each K/V tile staged in LDS serves all
-// of them; wavefront w owns rows 32 w .. 32 w + 31 as two 16-row blocks.
+// Work group = (query tile, kv head g, request b), 4 wavefronts, on a 1-D
+// grid laid out for the per-XCD L2s (see the work-item mapping below).  The
+// G query heads that share kv head g are stacked with the positions into 128
+// rows (row R = position * G + head), so each K/V tile staged in LDS serves
+// all of them; wavefront w owns rows 32 w .. 32 w + 31 as two 16-row blocks.
 // Per 64-key tile:
 //   * K and V rows are gathered through req_to_token into registers one tile
 //     ahead (slot ids one more tile ahead) and stored row-major into one of two
@@ -22,8 +23,9 @@
 //     16-key block for row l % 16, so a row's max needs two cross-lane steps;
 //   * softmax in base 2 against a lazily raised per-row reference (the
 //     accumulators are rescaled only when a logit exceeds it by more than
-//     kTau), weights rounded to bf16; the row sum adds the rounded weights, so
-//     the output is an exact convex combination of the bf16-weighted rows;
+//     kTau), weights rounded to bf16; the row sums of the rounded weights come
+//     from one more MFMA per 32 keys with an all-ones A operand, so the output
+//     is an exact convex combination of the bf16-weighted rows;
 //   * O^T += V^T P^T on v_mfma_f32_16x16x32_bf16: P^T is already in the
 //     B-operand layout (k = 8*(l/16) + e covers keys 4*(l/16) + e of two
 //     adjacent 16-key blocks), and V^T is read from the row-major V tile with
@@ -47,6 +49,7 @@ constexpr int kThreads = 256;
 constexpr int kRows = 128;       // (position, head) rows per work group
 constexpr int KT = 64;           // keys per tile
 constexpr float kTau = 8.0f;     // log2 headroom before the accumulators are rescaled
+constexpr int kXcds = 8;         // accelerator dies a launch is dealt across
 
 __device__ __forceinline__ uint4 load16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
@@ -65,7 +68,7 @@ struct PShape {
 };
 
 template <int D, int G>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillLaunch p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(const PrefillLaunch p) {
   using S = PShape<D>;
   constexpr int BQ = kRows / G;   // query positions per work group
   constexpr int NS = S::kSteps;
@@ -74,9 +77,22 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillLaunch p
   __shared__ __align__(16) uint16_t sK[2][KT * S::kKRow];
   __shared__ __align__(16) uint16_t sV[2][KT * S::kVRow];
 
-  const int qt = blockIdx.x;
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
+  // Work item of this work group.  Consecutive work groups are dealt to the
+  // 8 XCDs in turn, and each XCD has its own L2, so the linear id is remapped
+  // to keep every query tile of one (kv head, request) group on one XCD: the
+  // group's K/V tiles then come from HBM once and from that L2 for the other
+  // query tiles.  Groups are spread over the XCDs round robin, and within a
+  // group the tiles with the most keys start first.
+  const int nq = p.max_q_len > 0 ? (p.max_q_len + BQ - 1) / BQ : 0;
+  const int ngroups = p.num_kv_heads * p.batch;
+  if (nq == 0) return;
+  const int xcd = blockIdx.x % kXcds;
+  const int j = blockIdx.x / kXcds;
+  const int grp = xcd + kXcds * (j / nq);
+  if (grp >= ngroups) return;  // padding of the last round; uniform
+  const int qt = nq - 1 - j % nq;
+  const int g = grp % p.num_kv_heads;
+  const int b = grp / p.num_kv_heads;
   const int q0 = p.qo_indptr[b];
   const int qb = p.qo_indptr[b + 1] - q0;
   const int p0 = qt * BQ;
@@ -144,11 +160,15 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillLaunch p
   const float qk_scale = p.sm_scale * kLog2e;
   const int lim_min = cofs + p0;   // smallest row limit of the work group
   f32x4 acc[2][NB];
-  float mref[2], lsum[2];
+  f32x4 lacc[2];     // row sums of the weights (all four entries of a lane equal)
+  float mref[2];
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     mref[rb] = -INFINITY;
-    lsum[rb] = 0.f;
+    lacc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int db = 0; db < NB; ++db) acc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -181,44 +201,46 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillLaunch p
       }
     }
 
-    const bool need_mask = t0 + KT - 1 > lim_min;   // uniform
+    // Causal mask (only tiles that reach past the first row's limit need it).
+    if (t0 + KT - 1 > lim_min) {   // uniform
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (t0 + 16 * tb + 4 * kb + q > lim[rb]) st[rb][tb][q] = -INFINITY;
+    }
     bf16x8 pop[2][2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      float sv[4][4];
-      float tmax = -INFINITY;
+      // Row max of the raw logits, scaled afterwards (the scale is positive).
+      float tmax = fmaxf(fmaxf(st[rb][0][0], st[rb][0][1]), fmaxf(st[rb][0][2], st[rb][0][3]));
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float s = st[rb][tb][q] * qk_scale;
-          if (need_mask && t0 + 16 * tb + 4 * kb + q > lim[rb]) s = -INFINITY;
-          sv[tb][q] = s;
-          tmax = fmaxf(tmax, s);
-        }
-      tmax = xor_max<16, kWave>(tmax);
+      for (int tb = 1; tb < 4; ++tb)
+        tmax = fmaxf(tmax, fmaxf(fmaxf(st[rb][tb][0], st[rb][tb][1]), fmaxf(st[rb][tb][2], st[rb][tb][3])));
+      tmax = xor_max<16, kWave>(tmax) * qk_scale;
       const bool raise = tmax > mref[rb] + kTau;
       if (__builtin_amdgcn_ballot_w64(raise) != 0) {   // uniform over the wavefront
         const float mnew = fmaxf(mref[rb], tmax);
         const float alpha = exp2f(mref[rb] - mnew);     // mref == -inf on the first tile: scales zeros
         mref[rb] = mnew;
-        lsum[rb] *= alpha;
+        lacc[rb] *= alpha;
 #pragma unroll
         for (int db = 0; db < NB; ++db) acc[rb][db] *= alpha;
       }
-      float psum = 0.f;
+      const float moff = -mref[rb];
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
         bf16x8 v;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const __bf16 w = (__bf16)__builtin_amdgcn_exp2f(sv[2 * k2 + e / 4][e % 4] - mref[rb]);
-          psum += (float)w;
-          v[e] = w;
-        }
+        for (int e = 0; e < 8; ++e)
+          v[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(st[rb][2 * k2 + e / 4][e % 4], qk_scale, moff));
         pop[rb][k2] = v;
+        // Row sums of the rounded weights on the matrix core: every row of the
+        // all-ones A operand yields the column sums of P^T.
+        lacc[rb] = mfma32k(ones, v, lacc[rb]);
       }
-      lsum[rb] += psum;
     }
 
     // O^T += V^T P^T: A = V^T[16 db + l16][keys], keys in the same order as P^T's k slots.
@@ -244,7 +266,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillLaunch p
   // acc[rb][db][q] = O^T[d = 16 db + 4 kb + q][row 16 rb + l16], relative to mref.
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
-    const float ltot = xor_sum<16, kWave>(lsum[rb]);
+    const float ltot = lacc[rb][0];
     const int R = 32 * wv + 16 * rb + l16;
     const int posl = R / G;
     if (posl >= npos) continue;
@@ -265,8 +287,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillLaunch p
 template <int D, int G>
 hipError_t launch_t(const PrefillLaunch& p, hipStream_t s, const Timing& t) {
   constexpr int BQ = kRows / G;
-  const int qtiles = (p.max_q_len + BQ - 1) / BQ;
-  return launch_kernel(prefill_kernel<D, G>, dim3(qtiles, p.num_kv_heads, p.batch), dim3(kThreads), s, t, p);
+  const int64_t nq = (p.max_q_len + BQ - 1) / BQ;
+  const int64_t groups = (int64_t)p.num_kv_heads * p.batch;
+  const int64_t blocks = kXcds * ((groups + kXcds - 1) / kXcds) * nq;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  return launch_kernel(prefill_kernel<D, G>, dim3((unsigned)blocks, 1, 1), dim3(kThreads), s, t, p);
 }
 
 }  // namespace

@@ -124,6 +124,8 @@ def _call_prefill(a):
     (lambda a: setattr(a, "kv_stride_head", 60), 1, "kv_stride_head"),
     (lambda a: setattr(a, "o_stride_tok", 0), 1, "o_stride_tok"),
     (lambda a: setattr(a, "sm_scale", float("nan")), 1, "sm_scale"),
+    (lambda a: setattr(a, "sm_scale", -0.125), 1, "sm_scale"),
+    (lambda a: setattr(a, "sm_scale", 0.0), 1, "sm_scale"),
     (lambda a: setattr(a, "req_to_token_stride", 3), 1, "exceeds req_to_token_stride"),
     (lambda a: setattr(a, "num_slots", 0), 1, "num_slots"),
     (lambda a: setattr(a, "batch", -1), 1, "batch"),
