@@ -36,6 +36,8 @@
 #include "device_common.hpp"
 #include "kernel_launch.hpp"
 
+#include <type_traits>
+
 namespace astr {
 namespace {
 
@@ -176,92 +178,101 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   stash(0);
   __syncthreads();
 
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
-    const int t0 = it * KT;
-    const bool more = it + 1 < ntiles;   // uniform
-    if (more) {
-      gather(id_next);
-      id_next = load_id(t0 + 2 * KT);
-    }
-    const uint16_t* kt = sK[buf];
-    const uint16_t* vt = sV[buf];
-
-    // S^T blocks: st[rb][tb][q] = S^T[t0 + 16 tb + 4 kb + q][row 16 rb + l16].
-    f32x4 st[2][4];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      st[0][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      st[1][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < NS; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kt[(16 * tb + l16) * S::kKRow + 32 * ks + 8 * kb]);
-        st[0][tb] = mfma32k(a, qop[0][ks], st[0][tb]);
-        st[1][tb] = mfma32k(a, qop[1][ks], st[1][tb]);
+  // Tiles wholly below the first row's causal limit run without mask code,
+  // the remaining (diagonal) tiles with it.
+  auto run_tiles = [&](auto masked, int it_begin, int it_end) {
+    for (int it = it_begin; it < it_end; ++it) {
+      const int buf = it & 1;
+      const int t0 = it * KT;
+      const bool more = it + 1 < ntiles;   // uniform
+      if (more) {
+        gather(id_next);
+        id_next = load_id(t0 + 2 * KT);
       }
-    }
+      const uint16_t* kt = sK[buf];
+      const uint16_t* vt = sV[buf];
 
-    // Causal mask (only tiles that reach past the first row's limit need it).
-    if (t0 + KT - 1 > lim_min) {   // uniform
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (t0 + 16 * tb + 4 * kb + q > lim[rb]) st[rb][tb][q] = -INFINITY;
-    }
-    bf16x8 pop[2][2];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      // Row max of the raw logits, scaled afterwards (the scale is positive).
-      float tmax = fmaxf(fmaxf(st[rb][0][0], st[rb][0][1]), fmaxf(st[rb][0][2], st[rb][0][3]));
-#pragma unroll
-      for (int tb = 1; tb < 4; ++tb)
-        tmax = fmaxf(tmax, fmaxf(fmaxf(st[rb][tb][0], st[rb][tb][1]), fmaxf(st[rb][tb][2], st[rb][tb][3])));
-      tmax = xor_max<16, kWave>(tmax) * qk_scale;
-      const bool raise = tmax > mref[rb] + kTau;
-      if (__builtin_amdgcn_ballot_w64(raise) != 0) {   // uniform over the wavefront
-        const float mnew = fmaxf(mref[rb], tmax);
-        const float alpha = exp2f(mref[rb] - mnew);     // mref == -inf on the first tile: scales zeros
-        mref[rb] = mnew;
-        lacc[rb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < NB; ++db) acc[rb][db] *= alpha;
+      // S^T blocks: st[rb][tb][q] = S^T[t0 + 16 tb + 4 kb + q][row 16 rb + l16].
+      f32x4 st[2][4];
+  #pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        st[0][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        st[1][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+        for (int ks = 0; ks < NS; ++ks) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kt[(16 * tb + l16) * S::kKRow + 32 * ks + 8 * kb]);
+          st[0][tb] = mfma32k(a, qop[0][ks], st[0][tb]);
+          st[1][tb] = mfma32k(a, qop[1][ks], st[1][tb]);
+        }
       }
-      const float moff = -mref[rb];
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        bf16x8 v;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          v[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(st[rb][2 * k2 + e / 4][e % 4], qk_scale, moff));
-        pop[rb][k2] = v;
-        // Row sums of the rounded weights on the matrix core: every row of the
-        // all-ones A operand yields the column sums of P^T.
-        lacc[rb] = mfma32k(ones, v, lacc[rb]);
-      }
-    }
 
-    // O^T += V^T P^T: A = V^T[16 db + l16][keys], keys in the same order as P^T's k slots.
-#pragma unroll
-    for (int db = 0; db < NB; ++db) {
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)(vt + (32 * k2 + 4 * kb + (l16 >> 2)) * S::kVRow + 16 * db + 4 * (l16 & 3)));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)(vt + (32 * k2 + 16 + 4 * kb + (l16 >> 2)) * S::kVRow + 16 * db + 4 * (l16 & 3)));
-        const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        const bf16x8 aop = __builtin_bit_cast(bf16x8, both);
-        acc[0][db] = mfma32k(aop, pop[0][k2], acc[0][db]);
-        acc[1][db] = mfma32k(aop, pop[1][k2], acc[1][db]);
+      // Causal mask (only tiles that reach past the first row's limit need it).
+      if constexpr (decltype(masked)::value) {
+  #pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          const int thr = lim[rb] - t0 - 4 * kb;   // key 16 tb + q of this lane is visible iff <= thr
+  #pragma unroll
+          for (int tb = 0; tb < 4; ++tb)
+  #pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (16 * tb + q > thr) st[rb][tb][q] = -INFINITY;
+        }
       }
-    }
+      bf16x8 pop[2][2];
+  #pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        // Row max of the raw logits, scaled afterwards (the scale is positive).
+        float tmax = fmaxf(fmaxf(st[rb][0][0], st[rb][0][1]), fmaxf(st[rb][0][2], st[rb][0][3]));
+  #pragma unroll
+        for (int tb = 1; tb < 4; ++tb)
+          tmax = fmaxf(tmax, fmaxf(fmaxf(st[rb][tb][0], st[rb][tb][1]), fmaxf(st[rb][tb][2], st[rb][tb][3])));
+        tmax = xor_max<16, kWave>(tmax) * qk_scale;
+        const bool raise = tmax > mref[rb] + kTau;
+        if (__builtin_amdgcn_ballot_w64(raise) != 0) {   // uniform over the wavefront
+          const float mnew = fmaxf(mref[rb], tmax);
+          const float alpha = exp2f(mref[rb] - mnew);     // mref == -inf on the first tile: scales zeros
+          mref[rb] = mnew;
+          lacc[rb] *= alpha;
+  #pragma unroll
+          for (int db = 0; db < NB; ++db) acc[rb][db] *= alpha;
+        }
+        const float moff = -mref[rb];
+  #pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          bf16x8 v;
+  #pragma unroll
+          for (int e = 0; e < 8; ++e)
+            v[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(st[rb][2 * k2 + e / 4][e % 4], qk_scale, moff));
+          pop[rb][k2] = v;
+          // Row sums of the rounded weights on the matrix core: every row of the
+          // all-ones A operand yields the column sums of P^T.
+          lacc[rb] = mfma32k(ones, v, lacc[rb]);
+        }
+      }
 
-    if (more) stash(buf ^ 1);   // that buffer was last read before the previous barrier
-    __syncthreads();
-  }
+      // O^T += V^T P^T: A = V^T[16 db + l16][keys], keys in the same order as P^T's k slots.
+  #pragma unroll
+      for (int db = 0; db < NB; ++db) {
+  #pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4*)(vt + (32 * k2 + 4 * kb + (l16 >> 2)) * S::kVRow + 16 * db + 4 * (l16 & 3)));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4*)(vt + (32 * k2 + 16 + 4 * kb + (l16 >> 2)) * S::kVRow + 16 * db + 4 * (l16 & 3)));
+          const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          const bf16x8 aop = __builtin_bit_cast(bf16x8, both);
+          acc[0][db] = mfma32k(aop, pop[0][k2], acc[0][db]);
+          acc[1][db] = mfma32k(aop, pop[1][k2], acc[1][db]);
+        }
+      }
+
+      if (more) stash(buf ^ 1);   // that buffer was last read before the previous barrier
+      __syncthreads();
+    }
+  };
+  const int it_plain = min(ntiles, (lim_min + 1) / KT);
+  run_tiles(std::false_type{}, 0, it_plain);
+  run_tiles(std::true_type{}, it_plain, ntiles);
 
   // acc[rb][db][q] = O^T[d = 16 db + 4 kb + q][row 16 rb + l16], relative to mref.
 #pragma unroll
