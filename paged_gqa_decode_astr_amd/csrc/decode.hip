@@ -55,6 +55,7 @@ typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kTile = 16;       // keys per wavefront per tile (one MFMA column block)
+constexpr int kQBatchRows = 32;  // q rows (pieces x group heads) staged in LDS at a time
 constexpr float kTau = 8.0f;    // log2 headroom before the accumulators are rescaled
 
 __device__ __forceinline__ uint4 load16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -189,7 +190,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   __shared__ float sm_mref[kWaves][G];
   __shared__ float sm_mx[kWaves][G];
   __shared__ float sm_l[kWaves][G];
-  __shared__ __align__(16) uint16_t sm_q[2][G][QSTR];            // q rows of the current / next piece
+  constexpr int QB = kQBatchRows / G;   // pieces whose q rows are staged at a time
+  __shared__ __align__(16) uint16_t sm_q[QB][G][QSTR];           // q rows of the staged pieces
   __shared__ __align__(16) uint16_t sm_v[kWaves][kTile][S::kVRow];  // per-wavefront V tile
   __shared__ int32_t sm_kv[kKvStage];                              // window of kv_indptr starting at kv_base
 
@@ -269,15 +271,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       if constexpr (OFF32) return t < t_end ? id : -1;
       return id;
     };
-    // q rows of piece j's request: 16 bytes per thread for the first G*D/8 threads.
-    constexpr int kQThreads = G * D / 8;
-    auto q_chunk = [&](int j) -> uint4 {
-      const int t = min(tid, kQThreads - 1);
-      const int hh = t / (D / 8), dc = t % (D / 8);
-      return load16(p.q + (int64_t)(pt.b0 + j) * p.q_stride_tok + (int64_t)(g * G + hh) * p.q_stride_head + 8 * dc);
-    };
-    auto q_store = [&](int buf, const uint4& v) {
-      if (tid < kQThreads) *reinterpret_cast<uint4*>(&sm_q[buf][tid / (D / 8)][8 * (tid % (D / 8))]) = v;
+    // q rows of pieces [j0, j0 + nb) -> sm_q[0 .. nb).  The caller brackets
+    // this with barriers.
+    auto stage_q = [&](int j0, int nb) {
+      for (int t = tid; t < nb * G * (D / 8); t += kThreads) {
+        const int jj = t / (G * (D / 8));
+        const int hh = (t / (D / 8)) % G;
+        const int dc = t % (D / 8);
+        *reinterpret_cast<uint4*>(&sm_q[jj][hh][8 * dc]) =
+            load16(p.q + (int64_t)(pt.b0 + j0 + jj) * p.q_stride_tok + (int64_t)(g * G + hh) * p.q_stride_head + 8 * dc);
+      }
     };
 
     // Ping-pong pipeline over the wavefront's tile sequence c0, c1, c2, ...
@@ -290,6 +293,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     // together with it.  Tiles come in pairs within a piece, so buffer A
     // always holds even tiles and B odd ones and no register copy (which
     // would wait for its load) is ever needed.
+    // The q rows of the first batch of pieces are staged before any tile
+    // load, so waiting for them waits for nothing else.
+    stage_q(0, min(pt.n, QB));
     Cursor c0{0, 0, 0};
     settle(c0, pt, wv);
     Cursor c1 = c0;
@@ -298,14 +304,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     advance(c2, pt, wv);
     Cursor c3 = c2;
     advance(c3, pt, wv);
-    const uint4 q_first = q_chunk(0);
     int iA = id_at(c0);
     int iB = id_at(c1);
     Tile<D> A, Bt;
     load_tile<D, OFF32>(A, pv, iA, lane);
     iA = id_at(c2);
     load_tile<D, OFF32>(Bt, pv, iB, lane);
-    q_store(0, q_first);
     __syncthreads();
 
     float mref = -INFINITY, mx = -INFINITY, lsum = 0.f;
@@ -374,9 +378,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     };
 
     for (int j = 0; j < pt.n; ++j) {
-      const uint4 q_next = q_chunk(min(j + 1, pt.n - 1));
+      const int jj = j % QB;
+      if (j > 0 && jj == 0) {   // uniform: next batch of q rows (the previous merge ended with a barrier)
+        stage_q(j, min(pt.n - j, QB));
+        __syncthreads();
+      }
 #pragma unroll
-      for (int s = 0; s < NS; ++s) qop[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&sm_q[j & 1][hcol][32 * s + 8 * kb]));
+      for (int s = 0; s < NS; ++s) qop[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&sm_q[jj][hcol][32 * s + 8 * kb]));
       mref = -INFINITY;
       mx = -INFINITY;
       lsum = 0.f;
@@ -402,7 +410,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
           sm_l[wv][l16] = lsum;
         }
       }
-      q_store((j + 1) & 1, q_next);   // buffer last used by piece j - 1
       __syncthreads();
       const int slot = w + pt.b0 + j;
       for (int idx = tid; idx < G * D; idx += kThreads) {
