@@ -16,7 +16,8 @@
 // partial slot w + b.  Ranges are computed on the device from kv_indptr, so a
 // fixed grid stays valid when sequence lengths change.
 //
-// Inside a work group, 4 wavefronts take interleaved 16-key tiles of a piece.
+// Inside a work group, 4 wavefronts take interleaved 16-key tiles of a piece
+// (a piece of at most 64 keys goes whole to one wavefront).
 // Per tile and wavefront both products run on the matrix cores:
 //  * S^T = K Q^T with v_mfma_f32_16x16x32_bf16: A is the K tile as loaded
 //    (lane l holds 8 bf16 of key l % 16; four lanes cover 64 contiguous bytes
@@ -148,25 +149,52 @@ struct PieceTable {
   __device__ __forceinline__ int t_end(int j) const { return (int)(min(e1, (int64_t)kv[j + 1]) - kv[j]); }
 };
 
+// Pieces of at most kShortKeys keys are processed whole by one wavefront,
+// which writes their partial itself; longer pieces are shared by all
+// wavefronts and merged.  Piece j's owner (short) or first wavefront (long)
+// is (b0 + j) % kWaves, which spreads the extra tiles over the wavefronts.
+constexpr int kShortKeys = 4 * kTile;
+
+__device__ __forceinline__ bool short_piece(const PieceTable& pt, int j) {
+  return pt.t_end(j) - pt.t_begin(j) <= kShortKeys;
+}
+__device__ __forceinline__ int piece_lead(const PieceTable& pt, int j) { return (pt.b0 + j) % kWaves; }
+
 // A wavefront's position in its sequence of tiles: piece j, first key t of
-// the tile.  Wavefront wv takes tiles t_begin + kTile * (wv + kWaves * k) of
-// every piece, k = 0 .. nk - 1, with nk rounded up to an even count (the pad
-// tile is fully masked), so that tiles always come in pairs within a piece;
-// `stop` is the padded end.  j == n marks the end of the sequence.
+// the tile.  In a long piece wavefront wv takes tiles t_begin + kTile * (r +
+// kWaves * k) with r = (wv - lead) mod kWaves; in a short piece its owner takes
+// tiles t_begin + kTile * k.  The tile count is rounded up to an even number
+// (the pad tile is fully masked) so that tiles always come in pairs within a
+// piece; `stop` is the padded end, `stride` the step between the wavefront's
+// tiles.  j == n marks the end of the sequence.
 struct Cursor {
-  int j, t, stop;
+  int j, t, stop, stride;
 };
 
 __device__ __forceinline__ void settle(Cursor& c, const PieceTable& pt, int wv) {
   while (c.j < pt.n) {
-    const int tb = pt.t_begin(c.j) + kTile * wv;
+    const int tbeg = pt.t_begin(c.j);
     const int te = pt.t_end(c.j);
-    if (tb < te) {
-      int nk = (te - tb + kWaves * kTile - 1) / (kWaves * kTile);
-      nk += nk & 1;
-      c.t = tb;
-      c.stop = tb + nk * kWaves * kTile;
-      return;
+    const int lead = piece_lead(pt, c.j);
+    if (te - tbeg <= kShortKeys) {
+      if (wv == lead) {
+        int nk = (te - tbeg + kTile - 1) / kTile;
+        nk += nk & 1;
+        c.t = tbeg;
+        c.stride = kTile;
+        c.stop = tbeg + nk * kTile;
+        return;
+      }
+    } else {
+      const int tb = tbeg + kTile * ((wv - lead + kWaves) % kWaves);
+      if (tb < te) {
+        int nk = (te - tb + kWaves * kTile - 1) / (kWaves * kTile);
+        nk += nk & 1;
+        c.t = tb;
+        c.stride = kWaves * kTile;
+        c.stop = tb + nk * kWaves * kTile;
+        return;
+      }
     }
     ++c.j;
   }
@@ -174,7 +202,7 @@ __device__ __forceinline__ void settle(Cursor& c, const PieceTable& pt, int wv) 
 
 __device__ __forceinline__ void advance(Cursor& c, const PieceTable& pt, int wv) {
   if (c.j >= pt.n) return;
-  c.t += kWaves * kTile;
+  c.t += c.stride;
   if (c.t < c.stop) return;
   ++c.j;
   settle(c, pt, wv);
@@ -296,7 +324,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     // The q rows of the first batch of pieces are staged before any tile
     // load, so waiting for them waits for nothing else.
     stage_q(0, min(pt.n, QB));
-    Cursor c0{0, 0, 0};
+    Cursor c0{0, 0, 0, 0};
     settle(c0, pt, wv);
     Cursor c1 = c0;
     advance(c1, pt, wv);
@@ -379,10 +407,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 
     for (int j = 0; j < pt.n; ++j) {
       const int jj = j % QB;
-      if (j > 0 && jj == 0) {   // uniform: next batch of q rows (the previous merge ended with a barrier)
+      if (j > 0 && jj == 0) {   // uniform: next batch of q rows
+        __syncthreads();        // every wavefront holds the q rows of its earlier pieces
         stage_q(j, min(pt.n - j, QB));
         __syncthreads();
       }
+      const bool is_short = short_piece(pt, j);   // uniform
+      if (is_short && wv != piece_lead(pt, j)) continue;
 #pragma unroll
       for (int s = 0; s < NS; ++s) qop[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&sm_q[jj][hcol][32 * s + 8 * kb]));
       mref = -INFINITY;
@@ -394,6 +425,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       while (c0.j == j) {
         step(A, iA, iB);
         step(Bt, iB, iA);
+      }
+      if (is_short) {
+        // The owner writes the partial: o = acc / l, and (m, l) against the
+        // exact running max.
+        const float l_tot = xor_sum<16, kWave>(lsum);
+        const float mx_tot = xor_max<16, kWave>(mx);
+        if (l16 < G) {
+          const int64_t pidx = (int64_t)(g * G + l16) * p.num_partials + w + pt.b0 + j;
+          const float inv = 1.f / l_tot;
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+            *reinterpret_cast<float4*>(&p.o_part[pidx * D + 16 * b + 4 * kb]) =
+                make_float4(acc[b][0] * inv, acc[b][1] * inv, acc[b][2] * inv, acc[b][3] * inv);
+          if (kb == 0) {
+            p.ml_part[pidx * 2 + 0] = mx_tot * kLn2;
+            p.ml_part[pidx * 2 + 1] = l_tot * exp2f(mref - mx_tot);
+          }
+        }
+        continue;
       }
 
       // Wavefront totals over the four key groups of each column.
