@@ -148,9 +148,9 @@ astr::Timing timing_pair(void* const* events, int i) {
   return t;
 }
 
-// Thread groups for the combine kernel: enough that no group folds more than
-// two batches of 8 pieces for the request with the most pieces (from the
-// host copy of kv_indptr; the result does not depend on this choice).
+// Thread groups for the combine kernel: enough that each group folds one
+// batch of 8 pieces (at most 8 groups) for the request with the most pieces
+// (from the host copy of kv_indptr; the result does not depend on this).
 int32_t combine_groups(const astr_paged_args* a, int64_t total_keys, int64_t wh) {
   if (a->batch <= 0 || total_keys <= 0) return 1;
   const int64_t W = wh < total_keys ? wh : total_keys;
@@ -162,7 +162,7 @@ int32_t combine_groups(const astr_paged_args* a, int64_t total_keys, int64_t wh)
     const int64_t wl = ceil_div((int64_t)kv[b + 1] * W, total_keys) - 1;
     if (wl - wf + 1 > most) most = wl - wf + 1;
   }
-  const int64_t g = ceil_div(most, 16);
+  const int64_t g = ceil_div(most, 8);
   return (int32_t)(g < 1 ? 1 : (g > 8 ? 8 : g));
 }
 

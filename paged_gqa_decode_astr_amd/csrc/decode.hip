@@ -17,7 +17,7 @@
 // fixed grid stays valid when sequence lengths change.
 //
 // Inside a work group, 4 wavefronts take interleaved 16-key tiles of a piece
-// (a piece of at most 64 keys goes whole to one wavefront).
+// (a piece of at most 128 keys goes whole to one wavefront).
 // Per tile and wavefront both products run on the matrix cores:
 //  * S^T = K Q^T with v_mfma_f32_16x16x32_bf16: A is the K tile as loaded
 //    (lane l holds 8 bf16 of key l % 16; four lanes cover 64 contiguous bytes
@@ -153,7 +153,7 @@ struct PieceTable {
 // which writes their partial itself; longer pieces are shared by all
 // wavefronts and merged.  Piece j's owner (short) or first wavefront (long)
 // is (b0 + j) % kWaves, which spreads the extra tiles over the wavefronts.
-constexpr int kShortKeys = 4 * kTile;
+constexpr int kShortKeys = 8 * kTile;
 
 __device__ __forceinline__ bool short_piece(const PieceTable& pt, int j) {
   return pt.t_end(j) - pt.t_begin(j) <= kShortKeys;
@@ -488,25 +488,38 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   }
 }
 
-// One work group per (request, query head) with kCombineGroups groups of D
-// threads (the host picks the group count from the longest request's piece
-// count; any count gives the same result up to rounding order).  Thread d of
-// group r folds pieces r, r + groups, ... of the request, w_first..w_last,
-// into (M, den, num) for output element d with an online log-sum-exp merge,
-// kBatch pieces at a time so that their loads are in flight together.  The
-// groups then merge through LDS in group order, and group 0 writes O (bf16,
-// round to nearest even) and lse = M + ln(den).
+// One work group per (request, kCombineHeads query heads) with
+// combine_groups groups of 64 threads (the host picks the group count from
+// the longest request's piece count; any count gives the same result up to
+// rounding order).  Thread t of a group owns four consecutive output
+// elements of one head (float4 loads) and folds pieces r, r + groups, ... of
+// the request, w_first..w_last (r = its group), into (M, den, num) with an
+// online log-sum-exp merge, kBatch pieces at a time so that their loads are
+// in flight together.  The groups then merge through LDS in group order, and
+// group 0 writes O (bf16, round to nearest even) and lse = M + ln(den).
 constexpr int kBatch = 8;
 constexpr int kMaxCombineGroups = 8;
+constexpr int kCombineGroupThreads = kWave;
+
+template <int D>
+struct CombineShape {
+  static constexpr int kHeads = kCombineGroupThreads * 4 / D;   // query heads per work group
+};
 
 template <int D, int G>
-__global__ __launch_bounds__(D * kMaxCombineGroups) void decode_combine_kernel(const DecodeLaunch p) {
-  __shared__ float s_part[kMaxCombineGroups - 1][3][D];
+__global__ __launch_bounds__(kCombineGroupThreads * kMaxCombineGroups) void decode_combine_kernel(const DecodeLaunch p) {
+  constexpr int HP = CombineShape<D>::kHeads;
+  __shared__ float4 s_num[kMaxCombineGroups - 1][kCombineGroupThreads];
+  __shared__ float s_m[kMaxCombineGroups - 1][kCombineGroupThreads];
+  __shared__ float s_den[kMaxCombineGroups - 1][kCombineGroupThreads];
   const int b = blockIdx.x;
-  const int h = blockIdx.y;
-  const int d = threadIdx.x % D;
-  const int grp = threadIdx.x / D;
-  const int ngrp = blockDim.x / D;
+  const int t = threadIdx.x % kCombineGroupThreads;
+  const int grp = threadIdx.x / kCombineGroupThreads;
+  const int ngrp = blockDim.x / kCombineGroupThreads;
+  const int h = blockIdx.y * HP + t / (D / 4);
+  const int d4 = 4 * (t % (D / 4));
+  const bool live = h < p.num_qo_heads;
+  const int hc = live ? h : p.num_qo_heads - 1;   // idle threads read a valid row
   const int64_t N = p.kv_indptr[p.batch];
   const int64_t x0 = p.kv_indptr[b];
   const int64_t x1 = (int64_t)p.kv_indptr[b + 1] - 1;
@@ -514,19 +527,21 @@ __global__ __launch_bounds__(D * kMaxCombineGroups) void decode_combine_kernel(c
   const int wf = (int)(((x0 + 1) * W + N - 1) / N - 1);
   const int wl = (int)(((x1 + 1) * W + N - 1) / N - 1);
   const int n = wl - wf + 1;
-  const int64_t base = (int64_t)h * p.num_partials + b + wf;
+  const int64_t base = (int64_t)hc * p.num_partials + b + wf;
   const float* ml = p.ml_part + base * 2;
-  const float* op = p.o_part + base * D + d;
-  float M = -INFINITY, den = 0.f, num = 0.f;
+  const float* op = p.o_part + base * D + d4;
+  float M = -INFINITY, den = 0.f;
+  float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int i0 = grp; i0 < n; i0 += kBatch * ngrp) {
-    float m[kBatch], l[kBatch], o[kBatch];
+    float m[kBatch], l[kBatch];
+    float4 o[kBatch];
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       const int pi = min(i0 + i * ngrp, n - 1);
       const float2 mlv = *reinterpret_cast<const float2*>(ml + 2 * pi);
       m[i] = mlv.x;
       l[i] = mlv.y;
-      o[i] = op[(int64_t)pi * D];
+      o[i] = *reinterpret_cast<const float4*>(op + (int64_t)pi * D);
     }
     float Mb = M;
 #pragma unroll
@@ -534,36 +549,47 @@ __global__ __launch_bounds__(D * kMaxCombineGroups) void decode_combine_kernel(c
       if (i0 + i * ngrp < n) Mb = fmaxf(Mb, m[i]);
     const float sc = expf(M - Mb);   // M == -inf on the first batch: scales zeros
     den *= sc;
-    num *= sc;
+    num.x *= sc; num.y *= sc; num.z *= sc; num.w *= sc;
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       if (i0 + i * ngrp >= n) continue;
       const float wgt = l[i] * expf(m[i] - Mb);
       den += wgt;
-      num = fmaf(wgt, o[i], num);
+      num.x = fmaf(wgt, o[i].x, num.x);
+      num.y = fmaf(wgt, o[i].y, num.y);
+      num.z = fmaf(wgt, o[i].z, num.z);
+      num.w = fmaf(wgt, o[i].w, num.w);
     }
     M = Mb;
   }
   if (ngrp > 1) {
     if (grp > 0) {
-      s_part[grp - 1][0][d] = M;
-      s_part[grp - 1][1][d] = den;
-      s_part[grp - 1][2][d] = num;
+      s_num[grp - 1][t] = num;
+      s_m[grp - 1][t] = M;
+      s_den[grp - 1][t] = den;
     }
     __syncthreads();
     if (grp > 0) return;
     for (int k = 0; k < ngrp - 1; ++k) {
-      const float mk = s_part[k][0][d];
+      const float mk = s_m[k][t];
       if (mk == -INFINITY) continue;   // group had no piece
       const float Mn = fmaxf(M, mk);
       const float a = expf(M - Mn), c = expf(mk - Mn);   // group 0 always holds piece 0: M is finite
-      den = den * a + s_part[k][1][d] * c;
-      num = num * a + s_part[k][2][d] * c;
+      const float4 nk = s_num[k][t];
+      den = den * a + s_den[k][t] * c;
+      num.x = num.x * a + nk.x * c;
+      num.y = num.y * a + nk.y * c;
+      num.z = num.z * a + nk.z * c;
+      num.w = num.w * a + nk.w * c;
       M = Mn;
     }
   }
-  p.o[(int64_t)b * p.o_stride_tok + (int64_t)h * p.o_stride_head + d] = f32_to_bf16_rne(num / den);
-  if (p.lse != nullptr && d == 0) p.lse[(int64_t)b * p.lse_stride_tok + h] = M + logf(den);
+  if (!live) return;
+  const float inv = 1.f / den;
+  const uint32_t w0 = (uint32_t)f32_to_bf16_rne(num.x * inv) | ((uint32_t)f32_to_bf16_rne(num.y * inv) << 16);
+  const uint32_t w1 = (uint32_t)f32_to_bf16_rne(num.z * inv) | ((uint32_t)f32_to_bf16_rne(num.w * inv) << 16);
+  *reinterpret_cast<uint2*>(p.o + (int64_t)b * p.o_stride_tok + (int64_t)h * p.o_stride_head + d4) = make_uint2(w0, w1);
+  if (p.lse != nullptr && d4 == 0) p.lse[(int64_t)b * p.lse_stride_tok + h] = M + logf(den);
 }
 
 template <int D, int G>
@@ -575,7 +601,9 @@ hipError_t launch_split_t(const DecodeLaunch& p, hipStream_t s, const Timing& t)
 
 template <int D, int G>
 hipError_t launch_combine_t(const DecodeLaunch& p, hipStream_t s, const Timing& t) {
-  return launch_kernel(decode_combine_kernel<D, G>, dim3(p.batch, p.num_qo_heads, 1), dim3(D * p.combine_groups), s, t, p);
+  constexpr int HP = CombineShape<D>::kHeads;
+  const dim3 grid(p.batch, (p.num_qo_heads + HP - 1) / HP, 1);
+  return launch_kernel(decode_combine_kernel<D, G>, grid, dim3(kCombineGroupThreads * p.combine_groups), s, t, p);
 }
 
 #define ASTR_DECODE_CASES(FN)                       \
