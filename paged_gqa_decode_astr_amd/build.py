@@ -70,11 +70,33 @@ def build(jobs: int | None = None, extra=(), verbose: bool = False) -> str:
     return LIB
 
 
+PROBES = os.path.join(PKG, "probes")
+
+
+def build_probes(verbose: bool = False):
+    """Standalone measurement programs (not part of the library): probes/<name>.hip -> probes/<name>."""
+    out = []
+    for f in sorted(os.listdir(PROBES)) if os.path.isdir(PROBES) else []:
+        if not f.endswith(".hip"):
+            continue
+        src = os.path.join(PROBES, f)
+        exe = os.path.join(PROBES, f[:-4])
+        cmd = [hipcc(), "-O3", "-std=c++17"] + HIP_FLAGS + [src, "-o", exe]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+        out.append(exe)
+        if verbose:
+            print(f"built {exe}")
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=None)
     args = ap.parse_args(argv)
     build(args.jobs, verbose=True)
+    build_probes(verbose=True)
 
 
 if __name__ == "__main__":
