@@ -198,3 +198,49 @@ def test_decode_runs_on_the_callers_stream():
     s.synchronize()
     ref_o, _ = oracle_of(inp)
     assert_close(o, ref_o, "side stream O")
+
+
+def test_decode_pool_beyond_32bit_offsets():
+    """Rows more than 4 GiB above the kv-head base take the 64-bit addressing path; results are
+    bit-identical to the same rows in a small pool (32-bit buffer path) and match the oracle."""
+    seq = np.array([300, 1, 777, 64, 129])
+    inp = build_paged_inputs(seq, 32, 8, 128, 4096, seed=21)
+    small = tensors.to_device(inp, DEV)
+    big_slots = (1 << 21) + 4096          # 2^21 slots x 2 KiB rows: > 4 GiB per pool
+    shift = big_slots - 4096              # small-pool slot s lives at s + shift
+    big = dict(small)
+    big["k_pool"] = torch.full((big_slots, 8, 128), float("nan"), dtype=torch.bfloat16, device=DEV)
+    big["v_pool"] = torch.full((big_slots, 8, 128), float("nan"), dtype=torch.bfloat16, device=DEV)
+    big["k_pool"][shift:] = small["k_pool"]
+    big["v_pool"][shift:] = small["v_pool"]
+    r2t = inp["req_to_token"].copy()
+    r2t[r2t >= 0] += shift
+    big["req_to_token"] = torch.from_numpy(r2t).to(DEV)
+    B, Hq, D = inp["q"].shape
+    announce("decode with a pool beyond 32-bit row offsets")
+    outs = []
+    for dev in (small, big):
+        o = torch.empty(B, Hq, D, dtype=torch.bfloat16, device=DEV)
+        lse = torch.empty(B, Hq, dtype=torch.float32, device=DEV)
+        tensors.run_decode(dev, o=o, lse=lse, workspace=tensors.decode_workspace(B, Hq, D, DEV, max_splits=7),
+                           num_splits=7)
+        torch.cuda.synchronize()
+        outs.append((o, lse))
+    del big
+    assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
+    assert torch.equal(outs[0][1], outs[1][1])
+    ref_o, ref_lse = oracle_of(inp)
+    assert_close(outs[1][0], ref_o, "64-bit pool O")
+    assert_close(outs[1][1], ref_lse, "64-bit pool lse", atol=1e-3, rtol=1e-4)
+
+
+@pytest.mark.parametrize("scale", [0.03, 0.5])
+def test_decode_other_softmax_scales(scale):
+    seq = np.array([900, 5, 1300, 64])
+    inp = build_paged_inputs(seq, 32, 8, 128, 4096, seed=33)
+    inp["sm_scale"] = scale
+    announce(f"decode sm_scale={scale}")
+    o, lse, _, _ = _decode(inp, num_splits=5)
+    ref_o, ref_lse = oracle_of(inp)
+    assert_close(o, ref_o, f"scale {scale} O")
+    assert_close(lse, ref_lse, f"scale {scale} lse", atol=1e-3, rtol=1e-4)

@@ -83,3 +83,16 @@ def test_prefill_rows_match_decode():
     ref_o, _ = oracle_of(dec)
     assert_close(o_pre, ref_o, "prefill q_len=1 O", ulp_check=False)
     assert_close(o_dec, ref_o, "decode O")
+
+
+@pytest.mark.parametrize("scale", [0.03, 0.5])
+def test_prefill_other_softmax_scales(scale):
+    seq = np.array([700, 90, 1300])
+    ql = np.array([200, 90, 77])
+    inp = build_paged_inputs(seq, 32, 8, 128, 4096, seed=55, q_lens=ql)
+    inp["sm_scale"] = scale
+    announce(f"prefill sm_scale={scale}")
+    o, lse = _prefill(inp)
+    ref_o, ref_lse = oracle_of(inp)
+    assert_close(o, ref_o, f"prefill scale {scale} O", ulp_check=False)
+    assert_close(lse, ref_lse, f"prefill scale {scale} lse", atol=2e-3, rtol=1e-4)
