@@ -221,28 +221,40 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       bf16x8 pop[2][2];
   #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
-        // Row max of the raw logits, scaled afterwards (the scale is positive).
-        float tmax = fmaxf(fmaxf(st[rb][0][0], st[rb][0][1]), fmaxf(st[rb][0][2], st[rb][0][3]));
+        // Exponents against the current reference: x = s - mref (base 2).  The
+        // common case needs only this lane's maximum: if no x exceeds kTau the
+        // reference stands and no cross-lane step is taken.  A NaN maximum
+        // (mref == -inf before the row's first visible key) also raises.
+        float x[16];
+        const float moff = -mref[rb];
   #pragma unroll
-        for (int tb = 1; tb < 4; ++tb)
-          tmax = fmaxf(tmax, fmaxf(fmaxf(st[rb][tb][0], st[rb][tb][1]), fmaxf(st[rb][tb][2], st[rb][tb][3])));
-        tmax = xor_max<16, kWave>(tmax) * qk_scale;
-        const bool raise = tmax > mref[rb] + kTau;
+        for (int i = 0; i < 16; ++i) x[i] = fmaf(st[rb][i / 4][i % 4], qk_scale, moff);
+        float lmax = x[0];
+  #pragma unroll
+        for (int i = 1; i < 15; i += 2) lmax = fmaxf(lmax, fmaxf(x[i], x[i + 1]));
+        lmax = fmaxf(lmax, x[15]);
+        const bool raise = !(lmax <= kTau);
         if (__builtin_amdgcn_ballot_w64(raise) != 0) {   // uniform over the wavefront
+          // Raise the reference of every row of the block to its running max.
+          float tmax = st[rb][0][0];
+  #pragma unroll
+          for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, st[rb][i / 4][i % 4]);
+          tmax = xor_max<16, kWave>(tmax) * qk_scale;
           const float mnew = fmaxf(mref[rb], tmax);
           const float alpha = exp2f(mref[rb] - mnew);     // mref == -inf on the first tile: scales zeros
           mref[rb] = mnew;
           lacc[rb] *= alpha;
   #pragma unroll
           for (int db = 0; db < NB; ++db) acc[rb][db] *= alpha;
+          const float moff2 = mnew == -INFINITY ? 0.f : -mnew;   // no visible key yet: every weight 0
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) x[i] = fmaf(st[rb][i / 4][i % 4], qk_scale, moff2);
         }
-        const float moff = -mref[rb];
   #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
           bf16x8 v;
   #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            v[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(st[rb][2 * k2 + e / 4][e % 4], qk_scale, moff));
+          for (int e = 0; e < 8; ++e) v[e] = (__bf16)__builtin_amdgcn_exp2f(x[8 * k2 + e]);
           pop[rb][k2] = v;
           // Row sums of the rounded weights on the matrix core: every row of the
           // all-ones A operand yields the column sums of P^T.
