@@ -63,10 +63,9 @@ template <int D>
 struct PShape {
   static constexpr int kSteps = D / 32;                        // k-steps of S^T = K Q^T
   static constexpr int kDBlocks = D / 16;                      // 16-wide d blocks of O^T
-  static constexpr int kKRow = D + 8;                          // LDS row stride of the K tile (elements)
+  static constexpr int kKRow = D + 16;                         // LDS row stride of the K tile (elements)
   static constexpr int kVRow = D + 16;                         // LDS row stride of the V tile (elements)
-  static constexpr int kThreadsPerKey = kThreads / KT;         // 4 gather threads per key
-  static constexpr int kLoads = D / 8 / kThreadsPerKey;        // 16-byte K (and V) loads per thread per tile
+  static constexpr int kLoads = D / 32;                        // 16-byte K (and V) loads per thread per tile (4 threads per key)
 };
 
 template <int D, int G>
@@ -113,11 +112,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int l16 = lane & 15;
   const int kb = lane >> 4;
 
-  // Gather role: thread t loads NL 16-byte chunks of key t / 4 (quarter t % 4
-  // of the head row).  Keys past kv_end re-read key kv_end - 1 (finite data;
-  // every row masks them).
-  const int gkey = tid / S::kThreadsPerKey;
-  const int gcol = (tid % S::kThreadsPerKey) * (NL * 8);
+  // Gather role: thread t = 8 u + j takes key 4 (u / 2) + u % 2 (j < 4) or
+  // the key two rows further (j >= 4); its load i is the 16-byte chunk
+  // 4 i + j % 4 of that key's head row.  A quad of lanes reads 64 contiguous
+  // bytes of one row, and each group of 8 lanes stores into two rows two
+  // apart, which with the row stride D + 16 fall into distinct LDS banks (as
+  // do the 16-row MFMA operand reads of the K tile).  Keys past kv_end
+  // re-read key kv_end - 1 (finite data; every row masks them).
+  const int gkey = 4 * (tid / 16) + (tid / 8) % 2 + 2 * ((tid % 8) / 4);
+  const int gcol = 8 * (tid % 4);
   const int64_t head_off = (int64_t)g * p.kv_stride_head + gcol;
   auto load_id = [&](int t0) -> int { return ids[min(t0 + gkey, kv_end - 1)]; };
   uint4 kreg[NL], vreg[NL];
@@ -125,15 +128,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int64_t off = (int64_t)id * p.kv_stride_slot + head_off;
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      kreg[i] = load16(p.k_pool + off + 8 * i);
-      vreg[i] = load16(p.v_pool + off + 8 * i);
+      kreg[i] = load16(p.k_pool + off + 32 * i);
+      vreg[i] = load16(p.v_pool + off + 32 * i);
     }
   };
   auto stash = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      *reinterpret_cast<uint4*>(&sK[buf][gkey * S::kKRow + gcol + 8 * i]) = kreg[i];
-      *reinterpret_cast<uint4*>(&sV[buf][gkey * S::kVRow + gcol + 8 * i]) = vreg[i];
+      *reinterpret_cast<uint4*>(&sK[buf][gkey * S::kKRow + gcol + 32 * i]) = kreg[i];
+      *reinterpret_cast<uint4*>(&sV[buf][gkey * S::kVRow + gcol + 32 * i]) = vreg[i];
     }
   };
 
