@@ -196,16 +196,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       const uint16_t* vt = sV[buf];
 
       // S^T blocks: st[rb][tb][q] = S^T[t0 + 16 tb + 4 kb + q][row 16 rb + l16].
+      // The K operands of key block tb + 1 are read from LDS while block tb's
+      // MFMAs run; the scheduling fences keep the compiler from pulling the
+      // reads back next to their first use, where each pair would wait out a
+      // full LDS latency.
       f32x4 st[2][4];
+      bf16x8 ka[2][NS];
+  #pragma unroll
+      for (int ks = 0; ks < NS; ++ks) ka[0][ks] = *reinterpret_cast<const bf16x8*>(&kt[l16 * S::kKRow + 32 * ks + 8 * kb]);
   #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
+        if (tb < 3) {
+  #pragma unroll
+          for (int ks = 0; ks < NS; ++ks)
+            ka[(tb + 1) & 1][ks] = *reinterpret_cast<const bf16x8*>(&kt[(16 * (tb + 1) + l16) * S::kKRow + 32 * ks + 8 * kb]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
         st[0][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
         st[1][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
   #pragma unroll
         for (int ks = 0; ks < NS; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kt[(16 * tb + l16) * S::kKRow + 32 * ks + 8 * kb]);
-          st[0][tb] = mfma32k(a, qop[0][ks], st[0][tb]);
-          st[1][tb] = mfma32k(a, qop[1][ks], st[1][tb]);
+          st[0][tb] = mfma32k(ka[tb & 1][ks], qop[0][ks], st[0][tb]);
+          st[1][tb] = mfma32k(ka[tb & 1][ks], qop[1][ks], st[1][tb]);
         }
       }
 
@@ -265,9 +277,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         }
       }
 
-      // O^T += V^T P^T: A = V^T[16 db + l16][keys], keys in the same order as P^T's k slots.
-  #pragma unroll
-      for (int db = 0; db < NB; ++db) {
+      // O^T += V^T P^T: A = V^T[16 db + l16][keys], keys in the same order as
+      // P^T's k slots; the operands of d block db + 1 are read while block
+      // db's MFMAs run (same fencing as for K).
+      auto vread = [&](int db, bf16x8 (&dst)[2]) {
   #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
           const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -275,9 +288,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
           const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (lds_s16x4*)(vt + (32 * k2 + 16 + 4 * kb + (l16 >> 2)) * S::kVRow + 16 * db + 4 * (l16 & 3)));
           const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          const bf16x8 aop = __builtin_bit_cast(bf16x8, both);
-          acc[0][db] = mfma32k(aop, pop[0][k2], acc[0][db]);
-          acc[1][db] = mfma32k(aop, pop[1][k2], acc[1][db]);
+          dst[k2] = __builtin_bit_cast(bf16x8, both);
+        }
+      };
+      bf16x8 va[2][2];
+      vread(0, va[0]);
+  #pragma unroll
+      for (int db = 0; db < NB; ++db) {
+        if (db + 1 < NB) vread(db + 1, va[(db + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          acc[0][db] = mfma32k(va[db & 1][k2], pop[0][k2], acc[0][db]);
+          acc[1][db] = mfma32k(va[db & 1][k2], pop[1][k2], acc[1][db]);
         }
       }
 
