@@ -244,3 +244,20 @@ def test_decode_other_softmax_scales(scale):
     ref_o, ref_lse = oracle_of(inp)
     assert_close(o, ref_o, f"scale {scale} O")
     assert_close(lse, ref_lse, f"scale {scale} lse", atol=1e-3, rtol=1e-4)
+
+
+@pytest.mark.parametrize("ns", [0, 1, 7])
+def test_decode_more_requests_than_one_kv_indptr_window(ns):
+    """B = 2600 short requests: a work group's range spans more requests than
+    one LDS window of kv_indptr holds (1023 pieces), so the window is
+    re-staged mid-range; with one work group per head every request goes
+    through the same work group."""
+    rng = np.random.default_rng(2600 + ns)
+    seq = rng.integers(1, 12, size=2600)
+    seq[::97] = 300          # a few long requests among them
+    inp = build_paged_inputs(seq, 8, 2, 64, 1 << 16, seed=17 + ns, flat_table=(ns == 7))
+    announce(f"decode B=2600 windows num_splits={ns} N={int(seq.sum())}")
+    o, lse, _, _ = _decode(inp, num_splits=ns)
+    ref_o, ref_lse = oracle_of(inp)
+    assert_close(o, ref_o, f"B=2600 ns={ns} O")
+    assert_close(lse, ref_lse, f"B=2600 ns={ns} lse", atol=1e-3, rtol=1e-4)

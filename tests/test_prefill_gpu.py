@@ -96,3 +96,16 @@ def test_prefill_other_softmax_scales(scale):
     ref_o, ref_lse = oracle_of(inp)
     assert_close(o, ref_o, f"prefill scale {scale} O", ulp_check=False)
     assert_close(lse, ref_lse, f"prefill scale {scale} lse", atol=2e-3, rtol=1e-4)
+
+
+def test_prefill_many_short_requests():
+    """B = 1500 requests with 1..40 new tokens on 1..300-key histories."""
+    rng = np.random.default_rng(1500)
+    seq = rng.integers(1, 300, size=1500)
+    ql = np.minimum(seq, rng.integers(1, 41, size=1500))
+    inp = build_paged_inputs(seq, 8, 2, 64, 1 << 19, seed=15, q_lens=ql)
+    announce(f"prefill B=1500 rows={int(ql.sum())}")
+    o, lse = _prefill(inp)
+    ref_o, ref_lse = oracle_of(inp)
+    assert_close(o, ref_o, "prefill B=1500 O", ulp_check=False)
+    assert_close(lse, ref_lse, "prefill B=1500 lse", atol=2e-3, rtol=1e-4)
