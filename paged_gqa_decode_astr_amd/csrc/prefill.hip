@@ -14,10 +14,13 @@
 // rows (row R = position * G + head), so each K/V tile staged in LDS serves
 // all of them; wavefront w owns rows 32 w .. 32 w + 31 as two 16-row blocks.
 // Per 64-key tile:
-//   * K and V rows are gathered through req_to_token into registers one tile
-//     ahead (slot ids one more tile ahead) and stored row-major into one of two
-//     LDS buffers, so a single barrier per tile separates producers and
-//     consumers;
+//   * K and V rows are gathered through req_to_token straight into LDS
+//     (global_load_lds, 16 bytes per lane) one tile ahead, slot ids one more
+//     tile ahead, into the other of two stage buffers, so a single wait and
+//     barrier per tile separates producers and consumers.  Rows are D
+//     elements, unpadded; the 16-byte chunk c of row r sits at chunk
+//     c ^ swz(r) (swz = 2 (r % 8) for D = 128), which keeps both the K operand
+//     reads and the transposing V reads free of bank conflicts;
 //   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (A = K rows from LDS, B = Q^T
 //     held in registers): lane l gets the logits of keys 4*(l/16)..+3 of each
 //     16-key block for row l % 16, so a row's max needs two cross-lane steps;
@@ -28,7 +31,7 @@
 //     is an exact convex combination of the bf16-weighted rows;
 //   * O^T += V^T P^T on v_mfma_f32_16x16x32_bf16: P^T is already in the
 //     B-operand layout (k = 8*(l/16) + e covers keys 4*(l/16) + e of two
-//     adjacent 16-key blocks), and V^T is read from the row-major V tile with
+//     adjacent 16-key blocks), and V^T is read from the V tile with
 //     two transposing LDS reads (ds_read_b64_tr_b16) that follow the same key
 //     order.
 // Output rows are normalised by the row sum and written as bf16 (round to
@@ -75,8 +78,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   constexpr int NS = S::kSteps;
   constexpr int NB = S::kDBlocks;
   constexpr int NL = S::kLoads;
-  __shared__ __align__(16) uint16_t sK[2][KT * S::kKRow];
-  __shared__ __align__(16) uint16_t sV[2][KT * S::kVRow];
+  // Two stages, each its own array, so that the compiler can tell the LDS
+  // DMA into one stage from the reads of the other.
+  __shared__ __align__(16) uint16_t sK0[KT * D];
+  __shared__ __align__(16) uint16_t sK1[KT * D];
+  __shared__ __align__(16) uint16_t sV0[KT * D];
+  __shared__ __align__(16) uint16_t sV1[KT * D];
 
   // Work item of this work group.  Consecutive work groups are dealt to the
   // 8 XCDs in turn, and each XCD has its own L2, so the linear id is remapped
@@ -112,38 +119,48 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int l16 = lane & 15;
   const int kb = lane >> 4;
 
-  // Gather role: thread t = 8 u + j takes key 4 (u / 2) + u % 2 (j < 4) or
-  // the key two rows further (j >= 4); its load i is the 16-byte chunk
-  // 4 i + j % 4 of that key's head row.  A quad of lanes reads 64 contiguous
-  // bytes of one row, and each group of 8 lanes stores into two rows two
-  // apart, which with the row stride D + 16 fall into distinct LDS banks (as
-  // do the 16-row MFMA operand reads of the K tile).  Keys past kv_end
-  // re-read key kv_end - 1 (finite data; every row masks them).
-  const int gkey = 4 * (tid / 16) + (tid / 8) % 2 + 2 * ((tid % 8) / 4);
-  const int gcol = 8 * (tid % 4);
-  const int64_t head_off = (int64_t)g * p.kv_stride_head + gcol;
-  auto load_id = [&](int t0) -> int { return ids[min(t0 + gkey, kv_end - 1)]; };
-  uint4 kreg[NL], vreg[NL];
-  auto gather = [&](int id) {
-    const int64_t off = (int64_t)id * p.kv_stride_slot + head_off;
+  // Gather: each tile row (key) is D bf16 in LDS, split into CPR 16-byte
+  // chunks stored XOR-swizzled (chunk c of row r at position c ^ swz(r)) so
+  // that the MFMA operand reads and the transposing V reads hit distinct
+  // banks.  Load instruction i of wavefront wv fills the 1 KB block of rows
+  // RPI (NI wv + i) .. + RPI - 1 straight from HBM (global_load_lds: lane l
+  // lands at block + 16 l), so lane l fetches row RPI (NI wv + i) + l / CPR,
+  // global chunk (l % CPR) ^ swz(row).  Keys past kv_end re-read key
+  // kv_end - 1 (finite data; every row masks them).
+  constexpr int CPR = D / 8;
+  constexpr int RPI = kWave / CPR;
+  constexpr int NI = KT / RPI / (kThreads / kWave);
+  auto swz = [](int r) { return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); };
+  const int grow0 = RPI * NI * wv + lane / CPR;
+  int gchunk[NI];
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      kreg[i] = load16(p.k_pool + off + 32 * i);
-      vreg[i] = load16(p.v_pool + off + 32 * i);
+  for (int i = 0; i < NI; ++i) gchunk[i] = (lane % CPR) ^ swz(grow0 + RPI * i);
+  const int64_t head_off = (int64_t)g * p.kv_stride_head;
+  int id_next[NI];
+  auto load_ids = [&](int t0) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) id_next[i] = ids[min(t0 + grow0 + RPI * i, kv_end - 1)];
+  };
+  auto gather = [&](uint16_t* kdst, uint16_t* vdst) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int64_t off = (int64_t)id_next[i] * p.kv_stride_slot + head_off + 8 * gchunk[i];
+      const int row0 = RPI * (NI * wv + i);
+      __builtin_amdgcn_global_load_lds(p.k_pool + off, (__attribute__((address_space(3))) void*)(kdst + row0 * D), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(p.v_pool + off, (__attribute__((address_space(3))) void*)(vdst + row0 * D), 16, 0, 0);
     }
   };
-  auto stash = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      *reinterpret_cast<uint4*>(&sK[buf][gkey * S::kKRow + gcol + 32 * i]) = kreg[i];
-      *reinterpret_cast<uint4*>(&sV[buf][gkey * S::kVRow + gcol + 32 * i]) = vreg[i];
-    }
+  // Every wavefront waits for its own loads of a stage, then the barrier
+  // makes the whole tile visible.
+  auto stage_ready = [&]() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
   };
 
-  // Tile 0 in flight, tile 1's slot ids behind it.
-  int id_next = load_id(0);
-  gather(id_next);
-  id_next = load_id(KT);
+  // Tile 0 into stage 0, tile 1's slot ids behind it.
+  load_ids(0);
+  gather(sK0, sV0);
+  load_ids(KT);
 
   // B operand of S^T = K Q^T: lane (r + 16 kb) holds Q[row r][32 ks + 8 kb .. +7] of each row block.
   bf16x8 qop[2][NS];
@@ -178,22 +195,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     for (int db = 0; db < NB; ++db) acc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  stash(0);
-  __syncthreads();
+  stage_ready();
 
   // Tiles wholly below the first row's causal limit run without mask code,
   // the remaining (diagonal) tiles with it.
-  auto run_tiles = [&](auto masked, int it_begin, int it_end) {
-    for (int it = it_begin; it < it_end; ++it) {
-      const int buf = it & 1;
+  auto tile = [&](auto masked, auto stage, int it) __attribute__((always_inline)) {
+    {
       const int t0 = it * KT;
       const bool more = it + 1 < ntiles;   // uniform
       if (more) {
-        gather(id_next);
-        id_next = load_id(t0 + 2 * KT);
+        if constexpr (decltype(stage)::value == 0) gather(sK1, sV1); else gather(sK0, sV0);
+        load_ids(t0 + 2 * KT);
       }
-      const uint16_t* kt = sK[buf];
-      const uint16_t* vt = sV[buf];
+      const uint16_t* kt = decltype(stage)::value == 0 ? sK0 : sK1;
+      const uint16_t* vt = decltype(stage)::value == 0 ? sV0 : sV1;
+      const int swk = swz(l16);                               // K operand rows 16 tb + l16
+      const int swv = swz(4 * kb + (l16 >> 2));               // V^T rows 32 k2 (+16) + 4 kb + l16 / 4
 
       // S^T blocks: st[rb][tb][q] = S^T[t0 + 16 tb + 4 kb + q][row 16 rb + l16].
       // The K operands of key block tb + 1 are read from LDS while block tb's
@@ -203,13 +220,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       f32x4 st[2][4];
       bf16x8 ka[2][NS];
   #pragma unroll
-      for (int ks = 0; ks < NS; ++ks) ka[0][ks] = *reinterpret_cast<const bf16x8*>(&kt[l16 * S::kKRow + 32 * ks + 8 * kb]);
+      for (int ks = 0; ks < NS; ++ks) ka[0][ks] = *reinterpret_cast<const bf16x8*>(&kt[l16 * D + 8 * ((4 * ks + kb) ^ swk)]);
   #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
         if (tb < 3) {
   #pragma unroll
           for (int ks = 0; ks < NS; ++ks)
-            ka[(tb + 1) & 1][ks] = *reinterpret_cast<const bf16x8*>(&kt[(16 * (tb + 1) + l16) * S::kKRow + 32 * ks + 8 * kb]);
+            ka[(tb + 1) & 1][ks] = *reinterpret_cast<const bf16x8*>(&kt[(16 * (tb + 1) + l16) * D + 8 * ((4 * ks + kb) ^ swk)]);
         }
         __builtin_amdgcn_sched_barrier(0);
         st[0][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -283,10 +300,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       auto vread = [&](int db, bf16x8 (&dst)[2]) {
   #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
+          const int vcol = 8 * ((2 * db + ((l16 & 3) >> 1)) ^ swv) + 4 * (l16 & 1);
           const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4*)(vt + (32 * k2 + 4 * kb + (l16 >> 2)) * S::kVRow + 16 * db + 4 * (l16 & 3)));
+              (lds_s16x4*)(vt + (32 * k2 + 4 * kb + (l16 >> 2)) * D + vcol));
           const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4*)(vt + (32 * k2 + 16 + 4 * kb + (l16 >> 2)) * S::kVRow + 16 * db + 4 * (l16 & 3)));
+              (lds_s16x4*)(vt + (32 * k2 + 16 + 4 * kb + (l16 >> 2)) * D + vcol));
           const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           dst[k2] = __builtin_bit_cast(bf16x8, both);
         }
@@ -304,9 +322,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         }
       }
 
-      if (more) stash(buf ^ 1);   // that buffer was last read before the previous barrier
-      __syncthreads();
+      stage_ready();   // the next stage is loaded; this one may be overwritten
     }
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  // Tile it lives in stage it % 2.
+  auto run_tiles = [&](auto masked, int it_begin, int it_end) {
+    int it = it_begin;
+    if (it < it_end && (it & 1)) tile(masked, S1{}, it++);
+    for (; it + 1 < it_end; it += 2) {
+      tile(masked, S0{}, it);
+      tile(masked, S1{}, it + 1);
+    }
+    if (it < it_end) tile(masked, S0{}, it);
   };
   const int it_plain = min(ntiles, (lim_min + 1) / KT);
   run_tiles(std::false_type{}, 0, it_plain);

@@ -13,7 +13,10 @@
 //   store<S, M>: 16-byte stores of a gathered tile; M = 0: thread t stores
 //                key t / 4 at chunks 4 (t % 4) + i (quarters of a row per
 //                thread); M = 1: threads 8u + j store keys 4 (u / 2) + u % 2
-//                and two rows further, chunks 4 i + j % 4.
+//                and two rows further, chunks 4 i + j % 4;
+//   k_read_swz, v_tr_swz: the same reads from unpadded rows (stride D)
+//                whose 16-byte chunk c of row r sits at chunk c ^ 2 (r % 8),
+//                the layout the direct global-to-LDS gather writes.
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -92,6 +95,49 @@ __global__ void store(uint32_t* out) {
   out[blockIdx.x * 256 + tid] = t[tid * 3];
 }
 
+
+__global__ void k_read_swz(uint32_t* out) {
+  __shared__ __align__(16) uint16_t t[kKeys * kD];
+  const int tid = threadIdx.x, l16 = tid & 15, kb = (tid & 63) >> 4;
+  for (int i = tid; i < kKeys * kD / 8; i += 256) reinterpret_cast<uint4*>(t)[i] = make_uint4(i, i, i, i);
+  __syncthreads();
+  const int sw = 2 * (l16 & 7);
+  uint32_t acc = 0;
+  for (int it = 0; it < kIters; ++it) {
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const uint4 a = *reinterpret_cast<const uint4*>(&t[(16 * tb + l16) * kD + 8 * (((4 * ks + kb) ^ sw) ^ (it & 1))]);
+        acc += a.x ^ a.y ^ a.z ^ a.w;
+      }
+    asm volatile("" ::: "memory");
+  }
+  out[blockIdx.x * 256 + tid] = acc;
+}
+
+__global__ void v_tr_swz(uint32_t* out) {
+  __shared__ __align__(16) uint16_t t[kKeys * kD];
+  const int tid = threadIdx.x, l16 = tid & 15, kb = (tid & 63) >> 4;
+  for (int i = tid; i < kKeys * kD / 8; i += 256) reinterpret_cast<uint4*>(t)[i] = make_uint4(i, i, i, i);
+  __syncthreads();
+  const int sw = 2 * ((4 * kb + (l16 >> 2)) & 7);
+  uint32_t acc = 0;
+  for (int it = 0; it < kIters; ++it) {
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const int col = 8 * ((2 * db + ((l16 & 3) >> 1)) ^ sw) + 4 * (l16 & 1);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + (32 * k2 + 4 * kb + (l16 >> 2)) * kD + col));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + (32 * k2 + 16 + 4 * kb + (l16 >> 2)) * kD + col));
+        acc += (uint32_t)(lo[0] ^ lo[1] ^ lo[2] ^ lo[3] ^ hi[0] ^ hi[1] ^ hi[2] ^ hi[3]) + (uint32_t)it;
+      }
+    asm volatile("" ::: "memory");
+  }
+  out[blockIdx.x * 256 + tid] = acc;
+}
+
 template <typename K>
 void run(const char* name, K kern, uint32_t* out) {
   hipEvent_t a, b;
@@ -124,6 +170,8 @@ int main() {
   run("store quarters (M=0), stride D+8", store<kD + 8, 0>, out);
   run("store quarters (M=0), stride D+16", store<kD + 16, 0>, out);
   run("store paired rows (M=1), stride D+16", store<kD + 16, 1>, out);
+  run("k_read, stride D, chunks XOR-swizzled", k_read_swz, out);
+  run("v_tr, stride D, chunks XOR-swizzled", v_tr_swz, out);
   CHECK(hipDeviceSynchronize());
   CHECK(hipFree(out));
   return 0;
