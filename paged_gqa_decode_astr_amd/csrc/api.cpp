@@ -128,9 +128,10 @@ int validate_common(const astr_paged_args* a, bool prefill, int64_t* total_keys)
 }
 
 // Bytes from a kv head's base to the end of that head's row in the last
-// slot: (num_slots - 1) * kv_stride_slot * 2 + head_dim * 2.  The decode
-// kernel takes 32-bit buffer offsets when this is at most kPoolRange32 (the
-// offsets above it are its out-of-range marker).
+// slot: (num_slots - 1) * kv_stride_slot * 2 + head_dim * 2.  The kernels
+// take 32-bit buffer offsets when this is at most kPoolRange32 (the decode
+// kernel's offsets above it are its out-of-range marker); prefill also needs
+// slot ids and row strides below 2^24 for its 24-bit multiply.
 constexpr int64_t kPoolRange32 = 0xFFFFF000;
 
 int64_t pool_range_bytes(const astr_paged_args* a) {
@@ -335,6 +336,9 @@ int astr_paged_prefill(const astr_paged_args* a, void* workspace, size_t workspa
   p.kv_indptr = a->kv_indptr;
   p.qo_indptr = a->qo_indptr;
   p.max_q_len = max_q;
+  const int64_t range = pool_range_bytes(a);
+  p.off32 = range <= kPoolRange32 && a->num_slots <= (int64_t(1) << 24) && a->kv_stride_slot * 2 < (int64_t(1) << 24);
+  p.pool_range = p.off32 ? (uint32_t)range : 0u;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = astr::launch_prefill(p, s, timing_pair(a->timing_events, 0));
   if (e != hipSuccess) return fail(ASTR_ERR_HIP, "prefill kernel launch: %s", hipGetErrorString(e));

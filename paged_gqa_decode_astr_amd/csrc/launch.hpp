@@ -48,6 +48,8 @@ struct PrefillLaunch {
   const int32_t* kv_indptr;
   const int32_t* qo_indptr;
   int32_t max_q_len;     // grid covers query positions [0, max_q_len)
+  bool off32;            // 32-bit buffer offsets: pool rows of a kv head within pool_range bytes, slot ids < 2^24
+  uint32_t pool_range;   // off32: (num_slots - 1) * kv_stride_slot * 2 + head_dim * 2
 };
 
 // Optional events stamped by the dispatch itself at the kernel's start and

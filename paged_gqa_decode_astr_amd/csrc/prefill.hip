@@ -66,18 +66,16 @@ template <int D>
 struct PShape {
   static constexpr int kSteps = D / 32;                        // k-steps of S^T = K Q^T
   static constexpr int kDBlocks = D / 16;                      // 16-wide d blocks of O^T
-  static constexpr int kKRow = D + 16;                         // LDS row stride of the K tile (elements)
-  static constexpr int kVRow = D + 16;                         // LDS row stride of the V tile (elements)
-  static constexpr int kLoads = D / 32;                        // 16-byte K (and V) loads per thread per tile (4 threads per key)
 };
 
-template <int D, int G>
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int D, int G, bool OFF32>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(const PrefillLaunch p) {
   using S = PShape<D>;
   constexpr int BQ = kRows / G;   // query positions per work group
   constexpr int NS = S::kSteps;
   constexpr int NB = S::kDBlocks;
-  constexpr int NL = S::kLoads;
   // Two stages, each its own array, so that the compiler can tell the LDS
   // DMA into one stage from the reads of the other.
   __shared__ __align__(16) uint16_t sK0[KT * D];
@@ -127,6 +125,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // lands at block + 16 l), so lane l fetches row RPI (NI wv + i) + l / CPR,
   // global chunk (l % CPR) ^ swz(row).  Keys past kv_end re-read key
   // kv_end - 1 (finite data; every row masks them).
+  // OFF32: buffer loads over the kv head's rows (and the request's slot ids)
+  // with 32-bit offsets, one 24-bit multiply-add per key; otherwise 64-bit
+  // global addresses.
   constexpr int CPR = D / 8;
   constexpr int RPI = kWave / CPR;
   constexpr int NI = KT / RPI / (kThreads / kWave);
@@ -136,18 +137,36 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
   for (int i = 0; i < NI; ++i) gchunk[i] = (lane % CPR) ^ swz(grow0 + RPI * i);
   const int64_t head_off = (int64_t)g * p.kv_stride_head;
+  __amdgpu_buffer_rsrc_t krs, vrs, irs;
+  uint32_t row_bytes = 0;
+  if constexpr (OFF32) {
+    krs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.k_pool + head_off), (short)0, (int)p.pool_range, 0x00020000);
+    vrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.v_pool + head_off), (short)0, (int)p.pool_range, 0x00020000);
+    irs = __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(ids), (short)0, 4 * kv_end, 0x00020000);
+    row_bytes = (uint32_t)(p.kv_stride_slot * 2);
+  }
   int id_next[NI];
   auto load_ids = [&](int t0) {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) id_next[i] = ids[min(t0 + grow0 + RPI * i, kv_end - 1)];
+    for (int i = 0; i < NI; ++i) {
+      const int t = min(t0 + grow0 + RPI * i, kv_end - 1);
+      if constexpr (OFF32) id_next[i] = __builtin_amdgcn_raw_buffer_load_b32(irs, 4 * t, 0, 0);
+      else id_next[i] = ids[t];
+    }
   };
   auto gather = [&](uint16_t* kdst, uint16_t* vdst) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int64_t off = (int64_t)id_next[i] * p.kv_stride_slot + head_off + 8 * gchunk[i];
       const int row0 = RPI * (NI * wv + i);
-      __builtin_amdgcn_global_load_lds(p.k_pool + off, (__attribute__((address_space(3))) void*)(kdst + row0 * D), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(p.v_pool + off, (__attribute__((address_space(3))) void*)(vdst + row0 * D), 16, 0, 0);
+      if constexpr (OFF32) {
+        const uint32_t voff = __umul24((uint32_t)id_next[i], row_bytes) + 16u * gchunk[i];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kdst + row0 * D), 16, voff, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vdst + row0 * D), 16, voff, 0, 0, 0);
+      } else {
+        const int64_t off = (int64_t)id_next[i] * p.kv_stride_slot + head_off + 8 * gchunk[i];
+        __builtin_amdgcn_global_load_lds(p.k_pool + off, (lds_void*)(kdst + row0 * D), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(p.v_pool + off, (lds_void*)(vdst + row0 * D), 16, 0, 0);
+      }
     }
   };
   // Every wavefront waits for its own loads of a stage, then the barrier
@@ -369,7 +388,8 @@ hipError_t launch_t(const PrefillLaunch& p, hipStream_t s, const Timing& t) {
   const int64_t groups = (int64_t)p.num_kv_heads * p.batch;
   const int64_t blocks = kXcds * ((groups + kXcds - 1) / kXcds) * nq;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  return launch_kernel(prefill_kernel<D, G>, dim3((unsigned)blocks, 1, 1), dim3(kThreads), s, t, p);
+  if (p.off32) return launch_kernel(prefill_kernel<D, G, true>, dim3((unsigned)blocks, 1, 1), dim3(kThreads), s, t, p);
+  return launch_kernel(prefill_kernel<D, G, false>, dim3((unsigned)blocks, 1, 1), dim3(kThreads), s, t, p);
 }
 
 }  // namespace

@@ -109,3 +109,37 @@ def test_prefill_many_short_requests():
     ref_o, ref_lse = oracle_of(inp)
     assert_close(o, ref_o, "prefill B=1500 O", ulp_check=False)
     assert_close(lse, ref_lse, "prefill B=1500 lse", atol=2e-3, rtol=1e-4)
+
+
+def test_prefill_pool_beyond_32bit_offsets():
+    """Rows more than 4 GiB above the kv-head base take the 64-bit global-address gather; the
+    results are bit-identical to the same rows in a small pool (32-bit buffer gather) and match
+    the oracle."""
+    seq = np.array([300, 70, 777, 129])
+    ql = np.array([40, 70, 200, 1])
+    inp = build_paged_inputs(seq, 32, 8, 128, 4096, seed=23, q_lens=ql)
+    small = tensors.to_device(inp, DEV)
+    big_slots = (1 << 21) + 4096          # 2^21 slots x 2 KiB rows: > 4 GiB per pool
+    shift = big_slots - 4096              # small-pool slot s lives at s + shift
+    big = dict(small)
+    big["k_pool"] = torch.full((big_slots, 8, 128), float("nan"), dtype=torch.bfloat16, device=DEV)
+    big["v_pool"] = torch.full((big_slots, 8, 128), float("nan"), dtype=torch.bfloat16, device=DEV)
+    big["k_pool"][shift:] = small["k_pool"]
+    big["v_pool"][shift:] = small["v_pool"]
+    r2t = inp["req_to_token"].copy()
+    r2t[r2t >= 0] += shift
+    big["req_to_token"] = torch.from_numpy(r2t).to(DEV)
+    rows, Hq, D = inp["q"].shape
+    announce("prefill with a pool beyond 32-bit row offsets")
+    outs = []
+    for dev in (small, big):
+        lse = torch.empty(rows, Hq, dtype=torch.float32, device=DEV)
+        o = tensors.run_prefill(dev, lse=lse)
+        torch.cuda.synchronize()
+        outs.append((o, lse))
+    del big
+    assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
+    assert torch.equal(outs[0][1], outs[1][1])
+    ref_o, ref_lse = oracle_of(inp)
+    assert_close(outs[1][0], ref_o, "64-bit pool prefill O", ulp_check=False)
+    assert_close(outs[1][1], ref_lse, "64-bit pool prefill lse", atol=2e-3, rtol=1e-4)
