@@ -18,6 +18,9 @@ Sources (the AstrAI commit-list pages; no code, tests or data are on them):
   kv_indptr as the prefix sum of seq_lens, the unified causal_offset, GQA head
   expansion in the fallback, split-KV partials (o_part, ml_part) merged by a
   combine kernel, and partial slots written without a memset.
+* [attention_backend.py @47b3ed4] -- commits page for
+  ``astrai/extension/attention_backend.py`` at commit 47b3ed4: the commit that
+  shares one write-then-gather K/V helper between backends (the KV append).
 
 Parity status of each function is listed in its module header.
 """
@@ -25,9 +28,11 @@ from .attention import (bf16_bits_to_f64, f64_to_bf16_bits, request_slots, paged
                         attention_over_range)
 from .partition import (DEFAULTS, plan_num_splits, active_groups, wg_bounds, piece_table, pieces_of_request,
                         split_partials, combine_partials, decode_via_splits)
+from .kv_append import new_token_slots, kv_append
 
 __all__ = [
     "bf16_bits_to_f64", "f64_to_bf16_bits", "request_slots", "paged_attention",
     "attention_over_range", "DEFAULTS", "plan_num_splits", "active_groups", "wg_bounds", "piece_table",
     "pieces_of_request", "split_partials", "combine_partials", "decode_via_splits",
+    "new_token_slots", "kv_append",
 ]

@@ -96,7 +96,7 @@ def _draw_seq_lens(cfg: Config, gen: torch.Generator) -> np.ndarray:
 
 def build_paged_inputs(seq_lens, num_qo_heads, num_kv_heads, head_dim, num_slots, seed,
                        q_lens=None, row_stride=None, peaky_keys=0, flat_table=False,
-                       poison_unused=True):
+                       poison_unused=True, new_tokens=None):
     """Build one batch of paged inputs.
 
     seq_lens: per-request KV length L_b.  q_lens: per-request number of query
@@ -104,6 +104,13 @@ def build_paged_inputs(seq_lens, num_qo_heads, num_kv_heads, head_dim, num_slots
     a fresh run of a random permutation of all pool slots, so requests never
     share a slot.  ``flat_table`` returns req_to_token as one flat list indexed
     by kv_indptr (row stride 0); otherwise a 2-D table padded with -1.
+
+    new_tokens: per-request count n_b (1 <= n_b <= L_b) of tokens whose K/V
+    are not yet in the pool.  The K/V values of the last n_b positions of each
+    request are then returned as ``k_new`` / ``v_new`` ([sum n_b, Hkv, D], in
+    request order) instead of being stored, and their slots keep the unused
+    fill; ``k_pool_full`` / ``v_pool_full`` hold the pools with every position
+    stored, for comparison.
     """
     seq_lens = np.asarray(seq_lens, dtype=np.int64)
     B = int(seq_lens.shape[0])
@@ -150,9 +157,27 @@ def build_paged_inputs(seq_lens, num_qo_heads, num_kv_heads, head_dim, num_slots
     fill = BF16_QNAN if poison_unused else 0
     k_pool = np.full((num_slots, num_kv_heads, head_dim), fill, dtype=np.uint16)
     v_pool = np.full((num_slots, num_kv_heads, head_dim), fill, dtype=np.uint16)
-    k_pool[slots_flat] = k_vals
-    v_pool[slots_flat] = v_vals
-    return {
+    extra = {}
+    if new_tokens is not None:
+        n_new = np.broadcast_to(np.asarray(new_tokens, dtype=np.int64), (B,))
+        if np.any(n_new < 1) or np.any(n_new > seq_lens):
+            raise ValueError("new_tokens must satisfy 1 <= n_b <= seq_len_b")
+        is_new = np.zeros(N, dtype=bool)
+        for b in range(B):
+            is_new[kv_indptr[b + 1] - n_new[b]: kv_indptr[b + 1]] = True
+        extra["k_pool_full"] = k_pool.copy()
+        extra["v_pool_full"] = v_pool.copy()
+        extra["k_pool_full"][slots_flat] = k_vals
+        extra["v_pool_full"][slots_flat] = v_vals
+        extra["k_new"] = k_vals[is_new].copy()
+        extra["v_new"] = v_vals[is_new].copy()
+        extra["new_indptr"] = np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32)
+        k_pool[slots_flat[~is_new]] = k_vals[~is_new]
+        v_pool[slots_flat[~is_new]] = v_vals[~is_new]
+    else:
+        k_pool[slots_flat] = k_vals
+        v_pool[slots_flat] = v_vals
+    return {**extra,
         "q": q, "k_pool": k_pool, "v_pool": v_pool,
         "req_to_token": req_to_token, "req_to_token_stride": stride,
         "kv_indptr": kv_indptr, "qo_indptr": qo_indptr,
