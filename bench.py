@@ -17,7 +17,9 @@ is for the dominant kernel (the split kernel), timed live with HIP events that
 the kernel's own dispatch stamps at its start and end (hipExtLaunchKernel).  `cpu_baseline`
 times the fp64 CPU oracle on the same workload.  `prefill` reports the ragged
 prefill kernel (B=8, prefix U{0..2048}, q_len U{1..512}) against the bf16
-MFMA peak.
+MFMA peak.  `append` times a decode step that first appends each request's new
+token to the pools: the standalone append kernel followed by decode, against
+the fused append + decode call.
 """
 from __future__ import annotations
 
@@ -86,6 +88,7 @@ def main(argv=None):
     ap.add_argument("--config", default="decode_b32", help="decode workload (tiny, decode_b32, long_b1, long_b4, ragged_b256)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget (0 = skip)")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-append", action="store_true", help="skip the KV append + decode leg")
     ap.add_argument("--probe", action="store_true", help="also measure torch copy / row-gather bandwidth ceilings")
     ap.add_argument("--num-splits", type=int, default=0, help="decode work groups per kv head (0 = library plan)")
     args = ap.parse_args(argv)
@@ -164,6 +167,47 @@ def main(argv=None):
                      "bytes_per_launch": int(split_bytes / args.steps),
                      "us_per_launch": round(float(split_ms.mean()) * 1e3, 2)},
     }
+
+    if not args.no_append:
+        log("[bench] append leg: KV append + decode, separate vs fused")
+        asets = tensors.decode_sets(args.config, args.sets, dev, num_splits=args.num_splits, new_tokens=True)
+        torch.cuda.synchronize()
+
+        def sep(k, ev_app=None):
+            _, d = asets[k % len(asets)]
+            tensors.run_append(d, timing_events=ev_app)
+            tensors.run_decode(d, o=d["o"], lse=d["lse"], workspace=d["ws"], num_splits=args.num_splits)
+
+        def fused(k):
+            _, d = asets[k % len(asets)]
+            tensors.run_decode_append(d, o=d["o"], lse=d["lse"], workspace=d["ws"], num_splits=args.num_splits)
+
+        legs = {}
+        for name, fn in (("separate", sep), ("fused", fused)):
+            for k in range(args.warmup):
+                fn(k)
+            torch.cuda.synchronize()
+            start.record()
+            for k in range(args.steps):
+                fn(k)
+            stop.record()
+            torch.cuda.synchronize()
+            legs[name] = start.elapsed_time(stop) / args.steps * 1e3
+        aev = [[HipEvent() for _ in range(2)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for k in range(args.steps):
+            sep(k, aev[k])
+        torch.cuda.synchronize()
+        app_us = float(np.mean([e[0].elapsed_time(e[1]) for e in aev])) * 1e3
+        abytes = profiling.append_bytes(asets[0][0])
+        out["append"] = {
+            "workload": f"{args.config} with each request's last token appended first",
+            "us_per_call_separate": round(legs["separate"], 2), "us_per_call_fused": round(legs["fused"], 2),
+            "append_kernel_us": round(app_us, 2), "append_bytes": abytes,
+            "append_kernel_GBs": round(abytes / (app_us * 1e-6) / 1e9, 1),
+            "note": "separate = astr_kv_append then astr_paged_decode; fused = astr_paged_decode_append "
+                    "(same output bits); append_kernel_us from dispatch-stamped events of the standalone kernel"}
+        del asets
 
     if not args.no_prefill:
         log("[bench] prefill leg")

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define ASTR_ABI_VERSION 1
+#define ASTR_ABI_VERSION 2
 
 /* Default cap on work groups per kv head in an automatic decode plan. */
 #define ASTR_DEFAULT_MAX_SPLITS 256
@@ -166,6 +166,50 @@ int astr_paged_decode(const astr_paged_args* a, void* workspace, size_t workspac
 /* Ragged paged prefill with causal offset seq_len - q_len per request.
  * Needs no workspace (NULL / 0 allowed).  Returns astr_status. */
 int astr_paged_prefill(const astr_paged_args* a, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The K and V rows of a step's new tokens, bf16, [rows, Hkv, D]: element
+ * (row, g, d) at k_new[row * stride_tok + g * stride_head + d] (same for
+ * v_new).  Row r belongs to request b and is its i-th new token, with
+ * r = b for decode (one new token per request) or r = qo_indptr[b] + i for
+ * prefill (q_len new tokens).  16-byte aligned; strides are positive
+ * multiples of 8 elements. */
+typedef struct astr_new_kv {
+  const void* k_new;
+  const void* v_new;
+  int64_t stride_tok, stride_head;
+} astr_new_kv;
+
+/* KV append: writes the new tokens' K/V rows into the pools before they are
+ * attended, as the pages' shared write-then-gather helper does
+ * ([attention_backend.py @47b3ed4], commits page for
+ * astrai/extension/attention_backend.py at 47b3ed4, the commit extracting
+ * that helper).  kv_indptr already counts the new tokens, so new token i of
+ * request b (n_b new tokens) is position L_b - n_b + i and its rows go to
+ * pool slot req_to_token[row_b + L_b - n_b + i], every kv head.  n_b = 1 when
+ * a->qo_indptr is NULL (decode), else qo_indptr[b+1] - qo_indptr[b] with
+ * 1 <= n_b <= L_b.  Uses a's pools (written: they must be writable device
+ * memory despite the const in astr_paged_args), strides, num_slots,
+ * req_to_token, kv_indptr(+_host), qo_indptr(+_host), batch, num_kv_heads,
+ * head_dim (a multiple of 8) and max_q_len (> 0: fixed grid for up to that
+ * many new tokens per request, for graph capture); q, o, lse and
+ * num_qo_heads are ignored.  The new tokens' slots must be distinct (else the
+ * result is unspecified); a slot id outside [0, num_slots) is skipped, so
+ * nothing is written outside the pools.  No workspace.  a->timing_events,
+ * if set, takes the append kernel's start/end stamps in [0]/[1].  Returns
+ * astr_status; on error nothing is enqueued. */
+int astr_kv_append(const astr_paged_args* a, const astr_new_kv* nkv, void* stream);
+
+/* Fused KV append + paged decode, one launch fewer than astr_kv_append
+ * followed by astr_paged_decode, with the same result bit for bit (the same
+ * kernels' arithmetic on the same values).  The new token of request b is
+ * its last position L_b - 1 (kv_indptr counts it); its K/V row for kv head g
+ * is taken from nkv (row b) by the work group that owns that key, which also
+ * writes it into the pools at slot req_to_token[row_b + L_b - 1] (skipped for
+ * a slot outside [0, num_slots)).  The pool rows of the new tokens are not
+ * read.  Arguments, workspace and errors as astr_paged_decode; a->qo_indptr
+ * must be NULL.  Returns astr_status. */
+int astr_paged_decode_append(const astr_paged_args* a, const astr_new_kv* nkv, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* astr_last_error(void);

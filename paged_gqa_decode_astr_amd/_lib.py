@@ -25,7 +25,7 @@ ASTR_ERR_HIP = 4
 DEFAULT_MAX_SPLITS = 256
 
 EXPORTED = ("astr_workspace_size", "astr_plan_decode", "astr_paged_decode", "astr_paged_prefill",
-            "astr_last_error", "astr_abi_version")
+            "astr_kv_append", "astr_paged_decode_append", "astr_last_error", "astr_abi_version")
 
 
 class AstrError(RuntimeError):
@@ -50,6 +50,11 @@ class PagedArgs(ctypes.Structure):
         ("num_splits", ctypes.c_int32), ("max_q_len", ctypes.c_int32),
         ("timing_events", ctypes.c_void_p),
     ]
+
+
+class NewKV(ctypes.Structure):
+    _fields_ = [("k_new", ctypes.c_void_p), ("v_new", ctypes.c_void_p), ("stride_tok", ctypes.c_int64),
+                ("stride_head", ctypes.c_int64)]
 
 
 class DecodePlan(ctypes.Structure):
@@ -80,6 +85,11 @@ def load_library(path: str = LIB_PATH):
         f = getattr(lib, fn)
         f.restype = ctypes.c_int
         f.argtypes = [ctypes.POINTER(PagedArgs), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.astr_kv_append.restype = ctypes.c_int
+    lib.astr_kv_append.argtypes = [ctypes.POINTER(PagedArgs), ctypes.POINTER(NewKV), ctypes.c_void_p]
+    lib.astr_paged_decode_append.restype = ctypes.c_int
+    lib.astr_paged_decode_append.argtypes = [ctypes.POINTER(PagedArgs), ctypes.POINTER(NewKV), ctypes.c_void_p,
+                                             ctypes.c_size_t, ctypes.c_void_p]
     lib.astr_last_error.restype = ctypes.c_char_p
     lib.astr_last_error.argtypes = []
     lib.astr_abi_version.restype = ctypes.c_int
@@ -214,4 +224,97 @@ def astr_paged_prefill(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_hos
                         req_to_token_stride=req_to_token_stride, lse=lse, qo_indptr=qo_indptr,
                         qo_indptr_host=qo_indptr_host, max_q_len=max_q_len, timing_events=timing_events)
     _check(lib.astr_paged_prefill(ctypes.byref(a), None, 0, _stream_handle(stream)))
+    del keep
+
+
+def make_new_kv(k_new, v_new) -> NewKV:
+    """C view of the new tokens' rows k_new / v_new [rows, Hkv, D] bf16 (same strides)."""
+    import torch
+
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16 (got {t.dtype})")
+        if t.dim() != 3 or t.stride(2) != 1:
+            raise ValueError(f"{name} must be 3-D with a contiguous last dimension")
+    if k_new.stride() != v_new.stride() or k_new.shape != v_new.shape:
+        raise ValueError("k_new and v_new must have the same shape and strides")
+    n = NewKV()
+    n.k_new = _ptr(k_new)
+    n.v_new = _ptr(v_new)
+    n.stride_tok, n.stride_head = k_new.stride(0), k_new.stride(1)
+    return n
+
+
+def astr_kv_append(k_new, v_new, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host, *,
+                   req_to_token_stride, qo_indptr=None, qo_indptr_host=None, max_q_len=0, stream=None,
+                   timing_events=None):
+    """Write the new tokens' rows k_new / v_new [sum n_b, Hkv, D] bf16 into the pools (in place).
+
+    kv_indptr counts the new tokens; n_b = 1 per request without qo_indptr (decode), else
+    qo_indptr[b+1] - qo_indptr[b].  timing_events: optional 2 HipEvent (kernel start/end)."""
+    import torch
+
+    if timing_events is not None and len(timing_events) != 2:
+        raise ValueError("append timing_events takes 2 events (kernel start/end)")
+    for name, t in (("k_pool", k_pool), ("v_pool", v_pool)):
+        if t.dtype != torch.bfloat16 or t.dim() != 3 or t.stride(2) != 1:
+            raise TypeError(f"{name} must be a 3-D bfloat16 tensor with a contiguous last dimension")
+    if k_pool.stride() != v_pool.stride() or k_pool.shape != v_pool.shape:
+        raise ValueError("k_pool and v_pool must have the same shape and strides")
+    if k_new.shape[1:] != k_pool.shape[1:]:
+        raise ValueError(f"new rows {tuple(k_new.shape)} do not match the pool rows {tuple(k_pool.shape)}")
+    for name, t in (("req_to_token", req_to_token), ("kv_indptr", kv_indptr), ("qo_indptr", qo_indptr)):
+        if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
+            raise TypeError(f"{name} must be a contiguous int32 tensor")
+    lib = load_library()
+    kvh = _host_i32(kv_indptr_host)
+    qoh = _host_i32(qo_indptr_host)
+    rows = int(qoh[-1]) if qoh is not None else kv_indptr.numel() - 1
+    if k_new.shape[0] != rows:
+        raise ValueError(f"k_new has {k_new.shape[0]} rows; the new-token counts need {rows}")
+    a = PagedArgs()
+    a.batch = kv_indptr.numel() - 1
+    a.num_kv_heads = k_pool.shape[1]
+    a.num_qo_heads = k_pool.shape[1]
+    a.head_dim = k_pool.shape[2]
+    a.k_pool = _ptr(k_pool)
+    a.v_pool = _ptr(v_pool)
+    a.kv_stride_slot, a.kv_stride_head = k_pool.stride(0), k_pool.stride(1)
+    a.num_slots = k_pool.shape[0]
+    a.req_to_token = _ptr(req_to_token)
+    a.req_to_token_stride = int(req_to_token_stride)
+    a.kv_indptr = _ptr(kv_indptr)
+    a.kv_indptr_host = _np_ptr(kvh)
+    a.qo_indptr = _ptr(qo_indptr)
+    a.qo_indptr_host = _np_ptr(qoh)
+    a.max_q_len = int(max_q_len)
+    ev = None
+    if timing_events is not None:
+        ev = (ctypes.c_void_p * 2)(*[None if e is None else e.cuda_event for e in timing_events])
+        a.timing_events = ctypes.cast(ev, ctypes.c_void_p)
+    nkv = make_new_kv(k_new, v_new)
+    _check(lib.astr_kv_append(ctypes.byref(a), ctypes.byref(nkv), _stream_handle(stream)))
+    del kvh, qoh, ev
+
+
+def astr_paged_decode_append(q, k_new, v_new, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host, o,
+                             workspace, *, sm_scale, req_to_token_stride, lse=None, num_splits=0, stream=None,
+                             timing_events=None):
+    """Fused KV append + paged decode: writes k_new / v_new [B, Hkv, D] (request b's new token, its last
+    position) into the pools and decodes q [B, Hq, D] -> o (+ lse), bit-identical to astr_kv_append
+    followed by astr_paged_decode.  timing_events as astr_paged_decode."""
+    if timing_events is not None and len(timing_events) != 4:
+        raise ValueError("decode timing_events takes 4 events (split start/end, combine start/end)")
+    if k_new.shape[0] != q.shape[0] or k_new.shape[1:] != k_pool.shape[1:]:
+        raise ValueError(f"new rows {tuple(k_new.shape)} must be [B, Hkv, D] for q {tuple(q.shape)} and pool "
+                         f"{tuple(k_pool.shape)}")
+    lib = load_library()
+    a, keep = make_args(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host, o, sm_scale=sm_scale,
+                        req_to_token_stride=req_to_token_stride, lse=lse, num_splits=num_splits,
+                        timing_events=timing_events)
+    nkv = make_new_kv(k_new, v_new)
+    ws_ptr = _ptr(workspace)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.astr_paged_decode_append(ctypes.byref(a), ctypes.byref(nkv), ws_ptr, ws_bytes,
+                                        _stream_handle(stream)))
     del keep

@@ -223,10 +223,32 @@ int astr_plan_decode(const astr_paged_args* a, int32_t num_cus, astr_decode_plan
   return st == ASTR_OK ? ok() : st;
 }
 
-int astr_paged_decode(const astr_paged_args* a, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The new-token rows of an append: pointers, alignment and strides.
+int validate_new_kv(const astr_new_kv* nkv) {
+  if (nkv == nullptr) return fail(ASTR_ERR_INVALID_ARG, "new_kv is NULL");
+  if (nkv->k_new == nullptr || nkv->v_new == nullptr) return fail(ASTR_ERR_INVALID_ARG, "k_new and v_new must be set");
+  if (!aligned16(nkv->k_new) || !aligned16(nkv->v_new))
+    return fail(ASTR_ERR_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
+  if (nkv->stride_tok <= 0 || nkv->stride_tok % 8 != 0 || nkv->stride_head <= 0 || nkv->stride_head % 8 != 0)
+    return fail(ASTR_ERR_INVALID_ARG, "new_kv strides must be positive multiples of 8 elements (got %lld, %lld)",
+                (long long)nkv->stride_tok, (long long)nkv->stride_head);
+  return ASTR_OK;
+}
+
+// Decode, optionally with the fused append of one new token per request.
+int decode_impl(const astr_paged_args* a, const astr_new_kv* nkv, void* workspace, size_t workspace_bytes,
+                void* stream) {
   int64_t total = 0;
   int st = validate_common(a, false, &total);
   if (st != ASTR_OK) return st;
+  if (nkv != nullptr) {
+    st = validate_new_kv(nkv);
+    if (st != ASTR_OK) return st;
+  }
   if (a->qo_indptr != nullptr || a->qo_indptr_host != nullptr)
     return fail(ASTR_ERR_INVALID_ARG, "decode takes no qo_indptr (one query row per request)");
   if (a->batch == 0) return ok();
@@ -275,12 +297,103 @@ int astr_paged_decode(const astr_paged_args* a, void* workspace, size_t workspac
   p.o_part = static_cast<float*>(workspace);
   p.ml_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                        align256((int64_t)a->num_qo_heads * plan.num_partials * a->head_dim * 4));
+  p.k_new = nkv != nullptr ? static_cast<const uint16_t*>(nkv->k_new) : nullptr;
+  p.v_new = nkv != nullptr ? static_cast<const uint16_t*>(nkv->v_new) : nullptr;
+  p.new_stride_tok = nkv != nullptr ? nkv->stride_tok : 0;
+  p.new_stride_head = nkv != nullptr ? nkv->stride_head : 0;
+  p.num_slots = a->num_slots;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = astr::launch_decode_split(p, s, timing_pair(a->timing_events, 0));
   if (e != hipSuccess) return fail(ASTR_ERR_HIP, "split kernel launch: %s", hipGetErrorString(e));
   e = astr::launch_decode_combine(p, s, timing_pair(a->timing_events, 2));
   if (e != hipSuccess) return fail(ASTR_ERR_HIP, "combine kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int astr_paged_decode(const astr_paged_args* a, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(a, nullptr, workspace, workspace_bytes, stream);
+}
+
+int astr_paged_decode_append(const astr_paged_args* a, const astr_new_kv* nkv, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (nkv == nullptr) return fail(ASTR_ERR_INVALID_ARG, "new_kv is NULL");
+  return decode_impl(a, nkv, workspace, workspace_bytes, stream);
+}
+
+int astr_kv_append(const astr_paged_args* a, const astr_new_kv* nkv, void* stream) {
+  if (a == nullptr) return fail(ASTR_ERR_INVALID_ARG, "args is NULL");
+  int st = validate_new_kv(nkv);
+  if (st != ASTR_OK) return st;
+  if (a->batch < 0) return fail(ASTR_ERR_INVALID_ARG, "batch must be >= 0 (got %d)", a->batch);
+  if (a->num_kv_heads < 1) return fail(ASTR_ERR_INVALID_ARG, "num_kv_heads must be >= 1 (got %d)", a->num_kv_heads);
+  if (a->head_dim < 8 || a->head_dim % 8 != 0)
+    return fail(ASTR_ERR_INVALID_ARG, "head_dim must be a positive multiple of 8 (got %d)", a->head_dim);
+  if (a->batch > 65535) return fail(ASTR_ERR_INVALID_ARG, "batch (%d) must be <= 65535 (grid limit)", a->batch);
+  if (a->max_q_len < 0) return fail(ASTR_ERR_INVALID_ARG, "max_q_len must be >= 0");
+  if (a->batch == 0) return ok();
+  struct { const void* p; const char* name; } req[] = {
+      {a->k_pool, "k_pool"}, {a->v_pool, "v_pool"}, {a->req_to_token, "req_to_token"},
+      {a->kv_indptr, "kv_indptr"}, {a->kv_indptr_host, "kv_indptr_host"}};
+  for (auto& r : req)
+    if (r.p == nullptr) return fail(ASTR_ERR_INVALID_ARG, "%s is NULL", r.name);
+  if (!aligned16(a->k_pool) || !aligned16(a->v_pool)) return fail(ASTR_ERR_INVALID_ARG, "k_pool and v_pool must be 16-byte aligned");
+  if (a->kv_stride_slot <= 0 || a->kv_stride_slot % 8 != 0 || a->kv_stride_head <= 0 || a->kv_stride_head % 8 != 0)
+    return fail(ASTR_ERR_INVALID_ARG, "kv strides must be positive multiples of 8 elements");
+  if (a->num_slots < 1 || a->num_slots > (int64_t)INT32_MAX + 1)
+    return fail(ASTR_ERR_INVALID_ARG, "num_slots must be in [1, 2^31] (got %lld)", (long long)a->num_slots);
+  if (a->req_to_token_stride < 0) return fail(ASTR_ERR_INVALID_ARG, "req_to_token_stride must be >= 0");
+  if ((a->qo_indptr == nullptr) != (a->qo_indptr_host == nullptr))
+    return fail(ASTR_ERR_INVALID_ARG, "qo_indptr and qo_indptr_host must both be set or both be NULL");
+  const int32_t* kv = a->kv_indptr_host;
+  const int32_t* qo = a->qo_indptr_host;
+  if (kv[0] != 0) return fail(ASTR_ERR_INVALID_ARG, "kv_indptr[0] must be 0 (got %d)", kv[0]);
+  if (qo != nullptr && qo[0] != 0) return fail(ASTR_ERR_INVALID_ARG, "qo_indptr[0] must be 0 (got %d)", qo[0]);
+  int64_t max_new = 0;
+  for (int b = 0; b < a->batch; ++b) {
+    const int64_t L = (int64_t)kv[b + 1] - kv[b];
+    const int64_t n = qo != nullptr ? (int64_t)qo[b + 1] - qo[b] : 1;
+    if (n < 1 || n > L)
+      return fail(ASTR_ERR_INVALID_ARG, "request %d: need 1 <= new tokens <= seq_len (new %lld, seq_len %lld)", b,
+                  (long long)n, (long long)L);
+    if (a->req_to_token_stride > 0 && L > a->req_to_token_stride)
+      return fail(ASTR_ERR_INVALID_ARG, "request %d: seq_len %lld exceeds req_to_token_stride %lld", b, (long long)L,
+                  (long long)a->req_to_token_stride);
+    if (n > max_new) max_new = n;
+  }
+  if (a->max_q_len > 0) {
+    if (max_new > a->max_q_len)
+      return fail(ASTR_ERR_INVALID_ARG, "a request appends %lld tokens, more than max_q_len %d", (long long)max_new,
+                  a->max_q_len);
+    max_new = a->max_q_len;
+  }
+  if (max_new * a->num_kv_heads * (a->head_dim / 8) > (int64_t)INT32_MAX)
+    return fail(ASTR_ERR_INVALID_ARG, "too many new tokens per request for one launch");
+
+  astr::AppendLaunch p;
+  p.batch = a->batch;
+  p.num_kv_heads = a->num_kv_heads;
+  p.head_dim = a->head_dim;
+  p.max_new = (int32_t)max_new;
+  p.k_new = static_cast<const uint16_t*>(nkv->k_new);
+  p.v_new = static_cast<const uint16_t*>(nkv->v_new);
+  p.new_stride_tok = nkv->stride_tok;
+  p.new_stride_head = nkv->stride_head;
+  p.k_pool = static_cast<uint16_t*>(const_cast<void*>(a->k_pool));
+  p.v_pool = static_cast<uint16_t*>(const_cast<void*>(a->v_pool));
+  p.kv_stride_slot = a->kv_stride_slot;
+  p.kv_stride_head = a->kv_stride_head;
+  p.num_slots = a->num_slots;
+  p.req_to_token = a->req_to_token;
+  p.req_to_token_stride = a->req_to_token_stride;
+  p.kv_indptr = a->kv_indptr;
+  p.qo_indptr = a->qo_indptr;
+  const hipError_t e = astr::launch_kv_append(p, static_cast<hipStream_t>(stream), timing_pair(a->timing_events, 0));
+  if (e != hipSuccess) return fail(ASTR_ERR_HIP, "append kernel launch: %s", hipGetErrorString(e));
   return ok();
 }
 

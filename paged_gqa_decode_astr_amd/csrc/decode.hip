@@ -41,6 +41,16 @@
 //    weigh exactly zero; their loads re-read a valid key of the same request.
 // At the end of a piece the 4 wavefronts merge through LDS and one normalised
 // partial (o, m, l) per query head is written.
+//
+// Fused KV append (APPEND; [attention_backend.py @47b3ed4], the commit sharing
+// one write-then-gather K/V helper): the new token of request b is its last
+// key L_b - 1, and the work group whose range holds that key (for its kv head)
+// is the only one that reads it.  Before its first tile load, that work group
+// copies the token's K/V row from k_new / v_new into the pools; a work-group
+// barrier orders those stores before its own tile loads, which then read the
+// new rows like any other key.  The tile loop is the plain decode's; the
+// arithmetic sees the values a separate append followed by a decode would
+// read, so both give the same bits.
 #include "device_common.hpp"
 #include "kernel_launch.hpp"
 
@@ -208,7 +218,7 @@ __device__ __forceinline__ void advance(Cursor& c, const PieceTable& pt, int wv)
   settle(c, pt, wv);
 }
 
-template <int D, int G, bool OFF32>
+template <int D, int G, bool OFF32, bool APPEND>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void decode_split_kernel(const DecodeLaunch p) {
   using S = Shape<D>;
   constexpr int NS = S::kSteps;
@@ -268,6 +278,50 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     bnext = request_of(p.kv_indptr, B, pt.e0);
   }
 
+  // APPEND: requests bnext .. bnext + n_last - 1 have their last key in this
+  // range (those with kv_indptr[b + 1] <= e1; the request holding e0 ends
+  // after e0).  Task t copies 16 bytes of the K (wk = 0) or V (wk = 1) row of
+  // kv head g of request bnext + t / (D / 4).  The first kThreads tasks (one
+  // per thread, normally all of them) load now, so their round trip overlaps
+  // the q staging, and store after it; any others are copied right away.
+  [[maybe_unused]] int n_last = 0;
+  [[maybe_unused]] int32_t a_slot = -1;
+  [[maybe_unused]] uint4 a_val;
+  auto kvp = [&](int b) -> int64_t { return b <= staged ? (int64_t)sm_kv[b] : (int64_t)p.kv_indptr[b]; };
+  auto append_load = [&](int t, int32_t& slot, uint4& val) {
+    const int b = bnext + t / (2 * (D / 8));
+    const int64_t kb0 = kvp(b);
+    const int64_t L = kvp(b + 1) - kb0;
+    const int32_t* row = p.req_to_token + (p.req_to_token_stride > 0 ? (int64_t)b * p.req_to_token_stride : kb0);
+    slot = row[L - 1];
+    val = load16((((t / (D / 8)) & 1) ? p.v_new : p.k_new) + (int64_t)b * p.new_stride_tok +
+                 (int64_t)g * p.new_stride_head + 8 * (t % (D / 8)));
+  };
+  auto append_store = [&](int t, int32_t slot, const uint4& val) {
+    if (slot < 0 || (int64_t)slot >= p.num_slots) return;   // outside the pool: nothing is written
+    *reinterpret_cast<uint4*>(const_cast<uint16_t*>(((t / (D / 8)) & 1) ? p.v_pool : p.k_pool) +
+                              (int64_t)slot * p.kv_stride_slot + (int64_t)g * p.kv_stride_head + 8 * (t % (D / 8))) = val;
+  };
+  if constexpr (APPEND) {
+    // The requests ending in the range form a prefix of bnext, bnext + 1, ...:
+    // each lane tests one, a ballot counts them (64 per step; every
+    // wavefront finds the same count).
+    for (int base = bnext;; base += kWave) {
+      const int b = base + lane;
+      const uint64_t m = __builtin_amdgcn_ballot_w64(b < B && kvp(b + 1) <= pt.e1);
+      n_last += __builtin_popcountll(m);
+      if (m != ~0ull) break;
+    }
+    if (tid < n_last * 2 * (D / 8)) append_load(tid, a_slot, a_val);
+    for (int t = tid + kThreads; t < n_last * 2 * (D / 8); t += kThreads) {
+      int32_t slot;
+      uint4 val;
+      append_load(t, slot, val);
+      append_store(t, slot, val);
+    }
+  }
+  bool first_window = true;
+
   for (;;) {
     // Keep the window holding kv_indptr[bnext] and at least one entry after it.
     if (bnext - kv_base + 1 >= kKvStage) {
@@ -324,6 +378,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     // The q rows of the first batch of pieces are staged before any tile
     // load, so waiting for them waits for nothing else.
     stage_q(0, min(pt.n, QB));
+    if constexpr (APPEND) {
+      // The new rows are in the pools before any wavefront loads a tile
+      // (a work-group barrier orders the stores before the loads).
+      if (first_window && n_last > 0) {   // uniform over the work group
+        if (tid < n_last * 2 * (D / 8)) append_store(tid, a_slot, a_val);
+        __syncthreads();
+      }
+      first_window = false;
+    }
     Cursor c0{0, 0, 0, 0};
     settle(c0, pt, wv);
     Cursor c1 = c0;
@@ -595,8 +658,12 @@ __global__ __launch_bounds__(kCombineGroupThreads * kMaxCombineGroups) void deco
 template <int D, int G>
 hipError_t launch_split_t(const DecodeLaunch& p, hipStream_t s, const Timing& t) {
   const dim3 grid(p.num_splits, p.num_kv_heads, 1);
-  if (p.off32) return launch_kernel(decode_split_kernel<D, G, true>, grid, dim3(kThreads), s, t, p);
-  return launch_kernel(decode_split_kernel<D, G, false>, grid, dim3(kThreads), s, t, p);
+  if (p.k_new != nullptr) {
+    if (p.off32) return launch_kernel(decode_split_kernel<D, G, true, true>, grid, dim3(kThreads), s, t, p);
+    return launch_kernel(decode_split_kernel<D, G, false, true>, grid, dim3(kThreads), s, t, p);
+  }
+  if (p.off32) return launch_kernel(decode_split_kernel<D, G, true, false>, grid, dim3(kThreads), s, t, p);
+  return launch_kernel(decode_split_kernel<D, G, false, false>, grid, dim3(kThreads), s, t, p);
 }
 
 template <int D, int G>

@@ -29,6 +29,29 @@ struct DecodeLaunch {
   int32_t combine_groups;  // thread groups of the combine kernel (1..8)
   float* o_part;         // [Hq][P][D]
   float* ml_part;        // [Hq][P][2]
+  // Fused KV append (decode_append): the new token of request b is its last
+  // key; its rows come from k_new / v_new row b and are written to the pools.
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  int64_t new_stride_tok, new_stride_head;
+  int64_t num_slots;
+};
+
+// KV append: n_b new tokens per request (1 when qo_indptr is null), written
+// to pool slots req_to_token[row_b + L_b - n_b + i].
+struct AppendLaunch {
+  int32_t batch, num_kv_heads, head_dim;
+  int32_t max_new;       // grid covers new tokens [0, max_new) of each request
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  int64_t new_stride_tok, new_stride_head;
+  uint16_t* k_pool;
+  uint16_t* v_pool;
+  int64_t kv_stride_slot, kv_stride_head, num_slots;
+  const int32_t* req_to_token;
+  int64_t req_to_token_stride;
+  const int32_t* kv_indptr;
+  const int32_t* qo_indptr;   // null: one new token per request
 };
 
 struct PrefillLaunch {
@@ -63,6 +86,7 @@ struct Timing {
 hipError_t launch_decode_split(const DecodeLaunch& p, hipStream_t stream, const Timing& t);
 hipError_t launch_decode_combine(const DecodeLaunch& p, hipStream_t stream, const Timing& t);
 hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream, const Timing& t);
+hipError_t launch_kv_append(const AppendLaunch& p, hipStream_t stream, const Timing& t);
 
 // Whether a (head_dim, group) pair has a compiled kernel.
 bool decode_supported(int head_dim, int group);

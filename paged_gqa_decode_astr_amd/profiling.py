@@ -61,6 +61,14 @@ def split_kernel_bytes(inp):
     return N * Hkv * D * 2 * 2 + B * Hq * D * 2 + N * 4 + (B + 1) * 4
 
 
+def append_bytes(inp):
+    """Algorithmic HBM bytes of appending one new token per request: its K and V rows read once and
+    written once (every kv head), plus its slot id."""
+    B = inp["q"].shape[0]
+    Hkv, D = inp["num_kv_heads"], inp["head_dim"]
+    return B * Hkv * D * 2 * 2 * 2 + B * 4
+
+
 def sources_digest():
     return {p: hashlib.sha256(open(os.path.join(ROOT, p), "rb").read()).hexdigest() for p in TRAFFIC_SOURCES}
 

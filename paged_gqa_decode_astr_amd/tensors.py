@@ -25,6 +25,9 @@ def to_device(inp: dict, device="cuda") -> dict:
         "sm_scale": float(inp["sm_scale"]),
         "qo_indptr": None, "qo_indptr_host": None,
     }
+    if inp.get("k_new") is not None:
+        d["k_new"] = bf16_tensor(inp["k_new"], device)
+        d["v_new"] = bf16_tensor(inp["v_new"], device)
     if inp.get("qo_indptr") is not None:
         d["qo_indptr"] = torch.from_numpy(inp["qo_indptr"]).to(device)
         d["qo_indptr_host"] = np.ascontiguousarray(inp["qo_indptr"], dtype=np.int32)
@@ -54,6 +57,29 @@ def run_decode(dev: dict, o=None, lse=None, workspace=None, num_splits=0, stream
     return o
 
 
+def run_append(dev: dict, stream=None, timing_events=None, max_q_len=0):
+    """Write dev["k_new"] / dev["v_new"] into the device pools (one token per request without qo_indptr)."""
+    _lib.astr_kv_append(dev["k_new"], dev["v_new"], dev["k_pool"], dev["v_pool"], dev["req_to_token"],
+                        dev["kv_indptr"], dev["kv_indptr_host"], req_to_token_stride=dev["req_to_token_stride"],
+                        qo_indptr=dev["qo_indptr"], qo_indptr_host=dev["qo_indptr_host"], max_q_len=max_q_len,
+                        stream=stream, timing_events=timing_events)
+
+
+def run_decode_append(dev: dict, o=None, lse=None, workspace=None, num_splits=0, stream=None, timing_events=None):
+    """Fused append of dev["k_new"] / dev["v_new"] and decode."""
+    q = dev["q"]
+    if o is None:
+        o = torch.empty_like(q)
+    if workspace is None:
+        workspace = decode_workspace(q.shape[0], q.shape[1], q.shape[2], q.device,
+                                     max_splits=max(num_splits, 0))
+    _lib.astr_paged_decode_append(q, dev["k_new"], dev["v_new"], dev["k_pool"], dev["v_pool"], dev["req_to_token"],
+                                  dev["kv_indptr"], dev["kv_indptr_host"], o, workspace, sm_scale=dev["sm_scale"],
+                                  req_to_token_stride=dev["req_to_token_stride"], lse=lse, num_splits=num_splits,
+                                  stream=stream, timing_events=timing_events)
+    return o
+
+
 def run_prefill(dev: dict, o=None, lse=None, max_q_len=0, stream=None, timing_events=None):
     q = dev["q"]
     if o is None:
@@ -69,13 +95,14 @@ def bf16_to_f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().to(torch.float64).cpu().numpy()
 
 
-def decode_sets(config: str, nsets: int, device="cuda", num_splits: int = 0):
+def decode_sets(config: str, nsets: int, device="cuda", num_splits: int = 0, new_tokens: bool = False):
     """`nsets` independent seeded batches of a decode workload, resident on the device, each with its
-    own output, lse and workspace.  Rotating over them keeps each call's K/V out of the caches."""
+    own output, lse and workspace.  Rotating over them keeps each call's K/V out of the caches.
+    new_tokens: each request's last token is held back as k_new / v_new (for the append paths)."""
     from .workloads import make_inputs
     sets = []
     for t in range(nsets):
-        inp = make_inputs(config, t)
+        inp = make_inputs(config, t, new_tokens=1) if new_tokens else make_inputs(config, t)
         d = to_device(inp, device)
         B, Hq, D = inp["q"].shape
         d["o"] = torch.empty(B, Hq, D, dtype=torch.bfloat16, device=device)

@@ -25,7 +25,8 @@ def test_exports_every_declared_symbol(lib):
     assert declared == set(_lib.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.astr_abi_version() == 1
+    version = int(re.search(r"#define ASTR_ABI_VERSION (\d+)", header).group(1))
+    assert lib.astr_abi_version() == version
 
 
 def test_workspace_size_formula(lib):
@@ -185,3 +186,72 @@ def test_prefill_needs_qo_indptr():
     a, keep = _valid_decode_args()
     assert _call_prefill(a) == _lib.ASTR_ERR_INVALID_ARG
     assert "qo_indptr" in _lib.astr_last_error()
+
+
+# --------------------------------------------------------------------------- KV append validation
+
+def _new_kv(k=FAKE, v=FAKE, stride_tok=2 * 64, stride_head=64):
+    n = _lib.NewKV()
+    n.k_new, n.v_new, n.stride_tok, n.stride_head = k, v, stride_tok, stride_head
+    return n
+
+
+def _call_append(a, n):
+    lib = _lib.load_library()
+    return lib.astr_kv_append(ctypes.byref(a), None if n is None else ctypes.byref(n), None)
+
+
+def _call_decode_append(a, n, ws=FAKE, nbytes=1 << 30):
+    lib = _lib.load_library()
+    return lib.astr_paged_decode_append(ctypes.byref(a), None if n is None else ctypes.byref(n), ws, nbytes, None)
+
+
+@pytest.mark.parametrize("mutate,needle", [
+    (lambda a, n: setattr(n, "k_new", None), "k_new and v_new must be set"),
+    (lambda a, n: setattr(n, "v_new", FAKE + 2), "aligned"),
+    (lambda a, n: setattr(n, "stride_head", 12), "strides"),
+    (lambda a, n: setattr(n, "stride_tok", 0), "strides"),
+    (lambda a, n: setattr(a, "k_pool", None), "k_pool is NULL"),
+    (lambda a, n: setattr(a, "head_dim", 60), "head_dim"),
+    (lambda a, n: setattr(a, "kv_stride_slot", 100), "kv strides"),
+    (lambda a, n: setattr(a, "num_slots", 0), "num_slots"),
+    (lambda a, n: setattr(a, "req_to_token_stride", 3), "exceeds req_to_token_stride"),
+    (lambda a, n: setattr(a, "qo_indptr", FAKE), "both be set"),
+    (lambda a, n: setattr(a, "max_q_len", -1), "max_q_len"),
+])
+def test_append_rejects_bad_arguments(mutate, needle):
+    a, keep = _valid_decode_args()
+    n = _new_kv()
+    mutate(a, n)
+    assert _call_append(a, n) == _lib.ASTR_ERR_INVALID_ARG
+    assert needle in _lib.astr_last_error()
+
+
+@pytest.mark.parametrize("qo,max_q,needle", [((0, 0, 3), 0, "new tokens"), ((0, 4, 5), 0, "new tokens"),
+                                             ((1, 2, 3), 0, "qo_indptr[0]"), ((0, 2, 3), 1, "max_q_len")])
+def test_append_rejects_bad_new_counts(qo, max_q, needle):
+    a, keep = _valid_prefill_args(qo=qo)
+    a.max_q_len = max_q
+    assert _call_append(a, _new_kv()) == _lib.ASTR_ERR_INVALID_ARG
+    assert needle in _lib.astr_last_error()
+
+
+def test_append_null_new_kv_and_empty_batch():
+    a, keep = _valid_decode_args()
+    assert _call_append(a, None) == _lib.ASTR_ERR_INVALID_ARG
+    assert _call_decode_append(a, None) == _lib.ASTR_ERR_INVALID_ARG
+    a0, keep0 = _valid_decode_args((0,))
+    assert _call_append(a0, _new_kv()) == _lib.ASTR_OK
+    assert _call_decode_append(a0, _new_kv(), ws=None, nbytes=0) == _lib.ASTR_OK
+
+
+def test_decode_append_validates_like_decode():
+    a, keep = _valid_decode_args()
+    a.q = None
+    assert _call_decode_append(a, _new_kv()) == _lib.ASTR_ERR_INVALID_ARG
+    assert "q is NULL" in _lib.astr_last_error()
+    a, keep = _valid_decode_args()
+    assert _call_decode_append(a, _new_kv(stride_head=4)) == _lib.ASTR_ERR_INVALID_ARG
+    a, keep = _valid_decode_args()
+    a.num_splits = 4
+    assert _call_decode_append(a, _new_kv(), ws=None) == _lib.ASTR_ERR_WORKSPACE
