@@ -19,7 +19,8 @@ times the fp64 CPU oracle on the same workload.  `prefill` reports the ragged
 prefill kernel (B=8, prefix U{0..2048}, q_len U{1..512}) against the bf16
 MFMA peak.  `append` times a decode step that first appends each request's new
 token to the pools: the standalone append kernel followed by decode, against
-the fused append + decode call.
+the fused append + decode call.  `graph` times a 32-layer decode step made of
+per-layer calls against the same step captured once and replayed as a graph.
 """
 from __future__ import annotations
 
@@ -75,6 +76,68 @@ def cpu_baseline(inp, budget_s):
                            f"host has {len(os.sched_getaffinity(0))} cores"}
 
 
+def graph_leg(args, dev, layers_per_step=32, batches=(1, 4, 8, 16, 32), steps=20):
+    """Whole-step graph against eager calls: a decode step of `layers_per_step` layers (each with its own
+    pools, queries and outputs; seq_len ~ U{200..2000}, Hq 32 / Hkv 8, D 128) run as per-layer
+    astr_paged_decode calls from Python, and as one captured astr_decode_graph replayed per step."""
+    import torch
+    from paged_gqa_decode_astr_amd import _lib, tensors
+    from paged_gqa_decode_astr_amd.workloads import build_paged_inputs
+
+    res = []
+    s = torch.cuda.Stream()
+    for B in batches:
+        log(f"[bench] graph leg B={B}")
+        seq = np.random.default_rng(B).integers(200, 2001, size=B)
+        inp = build_paged_inputs(seq, 32, 8, 128, 1 << 16, seed=7000 + B)
+        layers = []
+        for _ in range(layers_per_step):
+            d = tensors.to_device(inp, dev)
+            d["o"] = torch.empty(B, 32, 128, dtype=torch.bfloat16, device=dev)
+            d["lse"] = torch.empty(B, 32, dtype=torch.float32, device=dev)
+            layers.append(d)
+        a0, keep = _lib.make_args(layers[0]["q"], layers[0]["k_pool"], layers[0]["v_pool"], layers[0]["req_to_token"],
+                                  layers[0]["kv_indptr"], layers[0]["kv_indptr_host"], layers[0]["o"], sm_scale=1.0,
+                                  req_to_token_stride=layers[0]["req_to_token_stride"])
+        ns = _lib.astr_plan_decode(a0, 0).num_splits
+        ws = tensors.decode_workspace(B, 32, 128, dev, max_splits=ns)
+        s.wait_stream(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+
+        def eager_step():
+            for d in layers:
+                tensors.run_decode(d, o=d["o"], lse=d["lse"], workspace=ws, num_splits=ns, stream=s)
+
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(3):
+            eager_step()
+        torch.cuda.synchronize()
+        t0.record(s)
+        for _ in range(steps):
+            eager_step()
+        t1.record(s)
+        torch.cuda.synchronize()
+        eager_us = t0.elapsed_time(t1) / steps * 1e3
+        g = _lib.DecodeGraph(layers, ws, num_splits=ns, stream=s)
+        for _ in range(3):
+            g.launch()
+        torch.cuda.synchronize()
+        t0.record(s)
+        for _ in range(steps):
+            g.launch()
+        t1.record(s)
+        torch.cuda.synchronize()
+        graph_us = t0.elapsed_time(t1) / steps * 1e3
+        g.close()
+        res.append({"batch": B, "eager_us_per_step": round(eager_us, 1), "graph_us_per_step": round(graph_us, 1),
+                    "speedup": round(eager_us / graph_us, 2)})
+        del layers, ws
+        torch.cuda.synchronize()
+    return {"workload": f"decode step of {layers_per_step} layers, each its own pools; seq_len ~ U{{200..2000}}, "
+                        "Hq 32 / Hkv 8, D 128; eager = per-layer astr_paged_decode calls from Python, graph = one "
+                        "astr_decode_graph launch per step", "steps": steps, "by_batch": res}
+
+
 def B_str(inp):
     return f"B={inp['q'].shape[0]}, {int(inp['kv_indptr'][-1])} keys"
 
@@ -89,6 +152,7 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget (0 = skip)")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-append", action="store_true", help="skip the KV append + decode leg")
+    ap.add_argument("--no-graph", action="store_true", help="skip the whole-step graph leg")
     ap.add_argument("--probe", action="store_true", help="also measure torch copy / row-gather bandwidth ceilings")
     ap.add_argument("--num-splits", type=int, default=0, help="decode work groups per kv head (0 = library plan)")
     args = ap.parse_args(argv)
@@ -208,6 +272,9 @@ def main(argv=None):
             "note": "separate = astr_kv_append then astr_paged_decode; fused = astr_paged_decode_append "
                     "(same output bits); append_kernel_us from dispatch-stamped events of the standalone kernel"}
         del asets
+
+    if not args.no_graph:
+        out["graph"] = graph_leg(args, dev)
 
     if not args.no_prefill:
         log("[bench] prefill leg")

@@ -211,6 +211,42 @@ int astr_kv_append(const astr_paged_args* a, const astr_new_kv* nkv, void* strea
 int astr_paged_decode_append(const astr_paged_args* a, const astr_new_kv* nkv, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* Whole-step decode graph ([attention_backend.py @47b3ed4], commits page for
+ * astrai/extension/attention_backend.py at 47b3ed4: the graph context with a
+ * warm-up -> capture -> replay lifecycle, one graph per batch size, every
+ * input at a fixed address, a live forward before capture).
+ *
+ * astr_decode_graph_create runs the decode of every layer once on `stream`
+ * (live run; it also validates each layer), then captures the same calls
+ * into a hipGraph and instantiates it.  layers[l] describes layer l's decode
+ * exactly as for astr_paged_decode; new_kv is NULL (plain decode) or an array
+ * of num_layers new-token rows (each layer's decode is then the fused
+ * append + decode of astr_paged_decode_append).  Every layer needs a fixed
+ * plan (num_splits > 0), no timing_events, and the same batch; all layers
+ * share `workspace`, which must hold the largest layer's plan.  `stream` must
+ * not be NULL (the null stream cannot be captured).
+ *
+ * The graph keeps the device pointers it was captured with: q, o, lse, pools,
+ * index arrays, new rows and workspace must stay allocated at the same
+ * addresses for as long as it is launched.  A launch recomputes the step from
+ * their current contents, so new sequence lengths in the device kv_indptr /
+ * req_to_token (same batch, each within the captured row stride) need no new
+ * capture.  The kv_indptr_host copies are read only during create.
+ * Ownership: the graph object (host memory, plus what the HIP runtime
+ * allocates to instantiate it) belongs to the caller and is released by
+ * astr_decode_graph_destroy.  On error *graph is NULL and nothing is
+ * captured (the live run may have been enqueued).  Each returns astr_status. */
+typedef struct astr_decode_graph astr_decode_graph;
+
+int astr_decode_graph_create(const astr_paged_args* layers, const astr_new_kv* new_kv, int32_t num_layers,
+                             void* workspace, size_t workspace_bytes, void* stream, astr_decode_graph** graph);
+
+/* Enqueues one replay of the captured step on `stream`. */
+int astr_decode_graph_launch(const astr_decode_graph* graph, void* stream);
+
+/* Releases the graph (NULL is a no-op). */
+int astr_decode_graph_destroy(astr_decode_graph* graph);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* astr_last_error(void);
 

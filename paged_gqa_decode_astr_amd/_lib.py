@@ -25,7 +25,8 @@ ASTR_ERR_HIP = 4
 DEFAULT_MAX_SPLITS = 256
 
 EXPORTED = ("astr_workspace_size", "astr_plan_decode", "astr_paged_decode", "astr_paged_prefill",
-            "astr_kv_append", "astr_paged_decode_append", "astr_last_error", "astr_abi_version")
+            "astr_kv_append", "astr_paged_decode_append", "astr_decode_graph_create", "astr_decode_graph_launch",
+            "astr_decode_graph_destroy", "astr_last_error", "astr_abi_version")
 
 
 class AstrError(RuntimeError):
@@ -90,6 +91,14 @@ def load_library(path: str = LIB_PATH):
     lib.astr_paged_decode_append.restype = ctypes.c_int
     lib.astr_paged_decode_append.argtypes = [ctypes.POINTER(PagedArgs), ctypes.POINTER(NewKV), ctypes.c_void_p,
                                              ctypes.c_size_t, ctypes.c_void_p]
+    lib.astr_decode_graph_create.restype = ctypes.c_int
+    lib.astr_decode_graph_create.argtypes = [ctypes.POINTER(PagedArgs), ctypes.POINTER(NewKV), ctypes.c_int32,
+                                             ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                             ctypes.POINTER(ctypes.c_void_p)]
+    lib.astr_decode_graph_launch.restype = ctypes.c_int
+    lib.astr_decode_graph_launch.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    lib.astr_decode_graph_destroy.restype = ctypes.c_int
+    lib.astr_decode_graph_destroy.argtypes = [ctypes.c_void_p]
     lib.astr_last_error.restype = ctypes.c_char_p
     lib.astr_last_error.argtypes = []
     lib.astr_abi_version.restype = ctypes.c_int
@@ -318,3 +327,52 @@ def astr_paged_decode_append(q, k_new, v_new, k_pool, v_pool, req_to_token, kv_i
     _check(lib.astr_paged_decode_append(ctypes.byref(a), ctypes.byref(nkv), ws_ptr, ws_bytes,
                                         _stream_handle(stream)))
     del keep
+
+
+class DecodeGraph:
+    """A captured multi-layer decode step (astr_decode_graph_*): warm-up, capture, replay.
+
+    layers: one dict per layer with the astr_paged_decode tensors (q, k_pool, v_pool, req_to_token,
+    kv_indptr, kv_indptr_host, o, and optionally lse, k_new / v_new for the fused append) plus
+    sm_scale and req_to_token_stride.  Every tensor must stay allocated while the graph is used;
+    a launch reads their current contents.  num_splits fixes the plan (required for capture)."""
+
+    def __init__(self, layers, workspace, *, num_splits, stream):
+        lib = load_library()
+        n = len(layers)
+        arr = (PagedArgs * n)()
+        keep = []
+        fused = [("k_new" in L and L["k_new"] is not None) for L in layers]
+        if any(fused) and not all(fused):
+            raise ValueError("either every layer or no layer takes new rows")
+        nkv = (NewKV * n)() if all(fused) else None
+        for i, L in enumerate(layers):
+            a, k = make_args(L["q"], L["k_pool"], L["v_pool"], L["req_to_token"], L["kv_indptr"],
+                             L["kv_indptr_host"], L["o"], sm_scale=L["sm_scale"],
+                             req_to_token_stride=L["req_to_token_stride"], lse=L.get("lse"), num_splits=num_splits)
+            arr[i] = a
+            keep.append(k)
+            if nkv is not None:
+                nkv[i] = make_new_kv(L["k_new"], L["v_new"])
+        self._stream = stream
+        handle = ctypes.c_void_p()
+        ws_bytes = workspace.numel() * workspace.element_size()
+        _check(lib.astr_decode_graph_create(arr, nkv, n, _ptr(workspace), ws_bytes, ctypes.c_void_p(stream.cuda_stream),
+                                            ctypes.byref(handle)))
+        self._handle = handle
+        self.num_layers = n
+
+    def launch(self, stream=None):
+        s = self._stream if stream is None else stream
+        _check(load_library().astr_decode_graph_launch(self._handle, ctypes.c_void_p(s.cuda_stream)))
+
+    def close(self):
+        if self._handle is not None and self._handle.value:
+            _check(load_library().astr_decode_graph_destroy(self._handle))
+        self._handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -15,12 +15,15 @@
 #include <mutex>
 #include <vector>
 
+#include "abi_internal.hpp"
 #include "astr_attn.h"
 #include "launch.hpp"
 
-namespace {
+namespace astr {
 
+namespace {
 thread_local char g_err[512] = "";
+}  // namespace
 
 int fail(int status, const char* fmt, ...) {
   va_list ap;
@@ -34,6 +37,15 @@ int ok() {
   g_err[0] = '\0';
   return ASTR_OK;
 }
+
+const char* last_error() { return g_err; }
+
+}  // namespace astr
+
+namespace {
+
+using astr::fail;
+using astr::ok;
 
 // Planner constants: work groups per CU (three 4-wavefront work groups fill
 // a CU at the head_dim-128 kernel's register budget), fewest keys per work
@@ -150,9 +162,17 @@ astr::Timing timing_pair(void* const* events, int i) {
 }
 
 // Thread groups for the combine kernel: enough that each group folds one
-// batch of 8 pieces (at most 8 groups) for the request with the most pieces
-// (from the host copy of kv_indptr; the result does not depend on this).
+// batch of 8 pieces (at most 8 groups) for the request with the most pieces.
+// The count decides the order in which pieces are folded, so it must not
+// depend on lengths when the plan is fixed (a captured graph replays with the
+// count it was captured with): then it follows from num_splits alone (a
+// request spans at most that many pieces).  An automatic plan takes it from
+// the host copy of kv_indptr.
 int32_t combine_groups(const astr_paged_args* a, int64_t total_keys, int64_t wh) {
+  if (a->num_splits > 0) {
+    const int64_t g = ceil_div(wh, 8);
+    return (int32_t)(g < 1 ? 1 : (g > 8 ? 8 : g));
+  }
   if (a->batch <= 0 || total_keys <= 0) return 1;
   const int64_t W = wh < total_keys ? wh : total_keys;
   const int32_t* kv = a->kv_indptr_host;
@@ -194,7 +214,7 @@ int plan_decode_impl(const astr_paged_args* a, int64_t total_keys, int32_t num_c
 
 extern "C" {
 
-const char* astr_last_error(void) { return g_err; }
+const char* astr_last_error(void) { return astr::last_error(); }
 
 int astr_abi_version(void) { return ASTR_ABI_VERSION; }
 
@@ -239,9 +259,11 @@ int validate_new_kv(const astr_new_kv* nkv) {
   return ASTR_OK;
 }
 
+}  // namespace
+
 // Decode, optionally with the fused append of one new token per request.
-int decode_impl(const astr_paged_args* a, const astr_new_kv* nkv, void* workspace, size_t workspace_bytes,
-                void* stream) {
+int astr::decode_impl(const astr_paged_args* a, const astr_new_kv* nkv, void* workspace, size_t workspace_bytes,
+                      void* stream) {
   int64_t total = 0;
   int st = validate_common(a, false, &total);
   if (st != ASTR_OK) return st;
@@ -311,18 +333,16 @@ int decode_impl(const astr_paged_args* a, const astr_new_kv* nkv, void* workspac
   return ok();
 }
 
-}  // namespace
-
 extern "C" {
 
 int astr_paged_decode(const astr_paged_args* a, void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_impl(a, nullptr, workspace, workspace_bytes, stream);
+  return astr::decode_impl(a, nullptr, workspace, workspace_bytes, stream);
 }
 
 int astr_paged_decode_append(const astr_paged_args* a, const astr_new_kv* nkv, void* workspace,
                              size_t workspace_bytes, void* stream) {
   if (nkv == nullptr) return fail(ASTR_ERR_INVALID_ARG, "new_kv is NULL");
-  return decode_impl(a, nkv, workspace, workspace_bytes, stream);
+  return astr::decode_impl(a, nkv, workspace, workspace_bytes, stream);
 }
 
 int astr_kv_append(const astr_paged_args* a, const astr_new_kv* nkv, void* stream) {

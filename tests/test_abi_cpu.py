@@ -255,3 +255,35 @@ def test_decode_append_validates_like_decode():
     a, keep = _valid_decode_args()
     a.num_splits = 4
     assert _call_decode_append(a, _new_kv(), ws=None) == _lib.ASTR_ERR_WORKSPACE
+
+
+# --------------------------------------------------------------------------- decode graph validation
+
+def _call_graph_create(layers, n, stream=FAKE, nkv=None):
+    lib = _lib.load_library()
+    out = ctypes.c_void_p(1234)
+    st = lib.astr_decode_graph_create(layers, nkv, n, FAKE, 1 << 30, stream, ctypes.byref(out))
+    return st, out
+
+
+def test_graph_create_rejects_bad_arguments():
+    arr = (_lib.PagedArgs * 2)()
+    a0, k0 = _valid_decode_args()
+    a1, k1 = _valid_decode_args()
+    a0.num_splits = a1.num_splits = 4
+    arr[0], arr[1] = a0, a1
+    st, out = _call_graph_create(arr, 0)
+    assert st == _lib.ASTR_ERR_INVALID_ARG and out.value is None
+    st, out = _call_graph_create(arr, 2, stream=None)
+    assert st == _lib.ASTR_ERR_INVALID_ARG and "non-null stream" in _lib.astr_last_error()
+    arr[1].num_splits = 0
+    st, out = _call_graph_create(arr, 2)
+    assert st == _lib.ASTR_ERR_INVALID_ARG and "fixed plan" in _lib.astr_last_error()
+    arr[1].num_splits = 4
+    arr[1].batch = 1
+    st, out = _call_graph_create(arr, 2)
+    assert st == _lib.ASTR_ERR_INVALID_ARG and "one graph per batch size" in _lib.astr_last_error()
+    lib = _lib.load_library()
+    assert lib.astr_decode_graph_create(arr, None, 2, FAKE, 1 << 30, FAKE, None) == _lib.ASTR_ERR_INVALID_ARG
+    assert lib.astr_decode_graph_launch(None, None) == _lib.ASTR_ERR_INVALID_ARG
+    assert lib.astr_decode_graph_destroy(None) == _lib.ASTR_OK
