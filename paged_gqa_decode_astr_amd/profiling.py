@@ -277,7 +277,9 @@ def main(argv=None):
         return _workload(args)
     if args.mode == "pmc":
         return _pmc(args)
-    return _trace(args, bench_args or ["--cpu-seconds", "0"])
+    # Default: the decode timing legs of bench.py only (its graph and append legs launch the same
+    # kernel at other shapes, which would enter the kernel's average).
+    return _trace(args, bench_args or ["--cpu-seconds", "0", "--no-graph", "--no-append"])
 
 
 if __name__ == "__main__":
