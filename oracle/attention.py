@@ -14,6 +14,14 @@ What is computed (the masked SDPA that the AstrAI pages describe):
 * [extension @6f67ba8], the commit adding the torch fallback with GQA head
   expansion: query head h reads kv head floor(h / (Hq / Hkv)) (repeat-interleave
   reading; the alternative h mod Hkv is not used).
+* [extension @6f67ba8], the commits unifying is_causal and causal_offset into
+  one causal offset that can be switched off, letting a boolean mask coexist
+  with it, and accepting a 2-D [batch, kv_len] or 3-D [batch, q_len, kv_len]
+  mask.  Readings: switched off (non_causal), every row sees all L_b keys; a
+  mask entry that is zero hides the key from that row on top of the causal
+  rule (2-D: one row per request, used by every query row); a row left with
+  no visible key outputs zeros with lse = -inf (the empty sum is taken as
+  zero weight everywhere).
 
 Precision: bf16 inputs are widened exactly to fp64; sm_scale is first rounded to
 fp32 (the precision the library receives it in), then widened.  Everything
@@ -79,27 +87,33 @@ def attention_over_range(qf, kf, vf, sigma, visible):
     qf [R, D], kf [T, D], vf [T, D] float64; visible [R, T] bool.
     Returns (o [R, D], m [R], l [R]) where m is the row max of the visible
     scaled logits, l = sum of exp(s - m) over visible keys, and
-    o = sum exp(s - m) v / l.  Rows with no visible key are not allowed.
+    o = sum exp(s - m) v / l.  A row with no visible key gets o = 0,
+    m = -inf and l = 0.
     """
     s = sigma * (qf @ kf.T)
     s_vis = np.where(visible, s, -np.inf)
-    m = s_vis.max(axis=1)
-    if not np.all(np.isfinite(m)):
-        raise ValueError("a row has no visible key")
-    p = np.where(visible, np.exp(s_vis - m[:, None]), 0.0)
+    empty = ~visible.any(axis=1)
+    m = np.where(empty, -np.inf, s_vis.max(axis=1, initial=-np.inf))
+    p = np.where(visible, np.exp(s_vis - np.where(empty, 0.0, m)[:, None]), 0.0)
     l = p.sum(axis=1)
-    o = (p @ vf) / l[:, None]
+    o = (p @ vf) / np.where(empty, 1.0, l)[:, None]
     return o, m, l
 
 
 def paged_attention(q_bits, k_pool_bits, v_pool_bits, req_to_token, req_to_token_stride,
-                    kv_indptr, sm_scale, qo_indptr=None):
+                    kv_indptr, sm_scale, qo_indptr=None, non_causal=False, mask=None):
     """Reference paged GQA attention.
 
     q_bits: [rows, Hq, D] bf16 bits; rows = B for decode (qo_indptr None) or
     qo_indptr[B] for prefill, in flat qo_indptr order.
     k_pool_bits, v_pool_bits: [num_slots, Hkv, D] bf16 bits.
-    Returns (o [rows, Hq, D] float64, lse [rows, Hq] float64 natural log).
+    non_causal: every query row sees all L_b keys (decode is the same either
+    way: its one row sees all keys).
+    mask: None, a 2-D [B, kv_len] or a 3-D [B, max_q_len, kv_len] array; key t
+    is hidden from row i of request b when mask[b, t] (2-D) or mask[b, i, t]
+    (3-D) is zero, on top of the causal rule.
+    Returns (o [rows, Hq, D] float64, lse [rows, Hq] float64 natural log);
+    rows with no visible key get o = 0 and lse = -inf.
     Requires 1 <= q_len_b <= seq_len_b for every request.
     """
     q_bits = np.asarray(q_bits)
@@ -127,10 +141,18 @@ def paged_attention(q_bits, k_pool_bits, v_pool_bits, req_to_token, req_to_token
         K = bf16_bits_to_f64(k_pool_bits[slots])   # [L, Hkv, D]
         V = bf16_bits_to_f64(v_pool_bits[slots])
         Q = bf16_bits_to_f64(q_bits[row0: row0 + qb])  # [qb, Hq, D]
-        visible = np.arange(L)[None, :] <= (c + np.arange(qb))[:, None]
+        if non_causal:
+            visible = np.ones((qb, L), dtype=bool)
+        else:
+            visible = np.arange(L)[None, :] <= (c + np.arange(qb))[:, None]
+        if mask is not None:
+            mk = np.asarray(mask)
+            rows_mask = mk[b, :L][None, :] if mk.ndim == 2 else mk[b, :qb, :L]
+            visible = visible & (rows_mask != 0)
         for h in range(Hq):
             g = h // group
             o, m, l = attention_over_range(Q[:, h, :], K[:, g, :], V[:, g, :], sigma, visible)
             out[row0: row0 + qb, h] = o
-            lse[row0: row0 + qb, h] = m + np.log(l)
+            with np.errstate(divide="ignore"):
+                lse[row0: row0 + qb, h] = np.where(l > 0, m + np.log(np.where(l > 0, l, 1.0)), -np.inf)
     return out, lse

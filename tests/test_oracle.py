@@ -74,11 +74,14 @@ def test_golden_attention_examples(golden_dir):
         v_pool = _pool_from_json(case["v_pool"], D, Hkv)
         q = f64_to_bits_exact(np.asarray(case["q"], dtype=np.float64))
         qo = None if case["qo_indptr"] is None else np.asarray(case["qo_indptr"], np.int32)
+        mask = None if case.get("mask") is None else np.asarray(case["mask"], np.uint8)
         o, lse = oracle.paged_attention(q, k_pool, v_pool, np.asarray(case["req_to_token"], np.int32),
                                         case["req_to_token_stride"], np.asarray(case["kv_indptr"], np.int32),
-                                        case["sm_scale"], qo_indptr=qo)
+                                        case["sm_scale"], qo_indptr=qo, non_causal=case.get("non_causal", False),
+                                        mask=mask)
         assert np.array_equal(o, np.asarray(case["o"], dtype=np.float64)), case["name"]
-        np.testing.assert_allclose(lse, np.asarray(case["lse"]), rtol=0, atol=1e-14, err_msg=case["name"])
+        want = np.asarray([[-np.inf if x is None else x for x in r] for r in case["lse"]])
+        np.testing.assert_allclose(lse, want, rtol=0, atol=1e-14, err_msg=case["name"])
 
 
 def test_golden_partition_examples(golden_dir):
