@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define ASTR_ABI_VERSION 2
+#define ASTR_ABI_VERSION 3
 
 /* Default cap on work groups per kv head in an automatic decode plan. */
 #define ASTR_DEFAULT_MAX_SPLITS 256
@@ -133,6 +133,25 @@ typedef struct astr_paged_args {
    * entries).  Elements may be NULL (not stamped).  Events stay owned by the
    * caller; leave this NULL in code that is captured into a graph. */
   void* const* timing_events;
+
+  /* Causal switch ([extension @6f67ba8], the commit unifying is_causal and
+   * causal_offset into one offset that can be turned off): 0 (default) ->
+   * prefill row i of request b sees keys 0 .. L_b - q_len_b + i; 1 -> every
+   * row sees all L_b keys.  Decode is the same either way. */
+  int32_t non_causal;
+  /* Optional boolean mask ([extension @6f67ba8], the commits letting a mask
+   * coexist with the causal offset and accepting 2-D [batch, kv_len] and 3-D
+   * [batch, q_len, kv_len] masks): uint8, key t of request b is hidden from
+   * its query row i when mask[b * mask_stride_req + i * mask_stride_row + t]
+   * is 0 -- on top of the causal rule.  mask_stride_row == 0 is a 2-D mask
+   * (one row per request, used by every query row); decode reads row 0.
+   * NULL: no mask.  The mask pointer and both strides must be multiples of
+   * 4 bytes; rows must hold max L_b entries (mask_stride_row >= max L_b for a
+   * 3-D mask, mask_stride_req >= max L_b for a 2-D one) and a 3-D request
+   * block max q_len rows; mask_stride_req < 2^31.  A query row left with no
+   * visible key outputs zeros and lse = -inf. */
+  const uint8_t* mask;
+  int64_t mask_stride_req, mask_stride_row;
 } astr_paged_args;
 
 typedef struct astr_decode_plan {

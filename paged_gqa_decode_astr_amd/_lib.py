@@ -50,6 +50,8 @@ class PagedArgs(ctypes.Structure):
         ("qo_indptr", ctypes.c_void_p), ("qo_indptr_host", ctypes.c_void_p),
         ("num_splits", ctypes.c_int32), ("max_q_len", ctypes.c_int32),
         ("timing_events", ctypes.c_void_p),
+        ("non_causal", ctypes.c_int32), ("mask", ctypes.c_void_p),
+        ("mask_stride_req", ctypes.c_int64), ("mask_stride_row", ctypes.c_int64),
     ]
 
 
@@ -139,8 +141,11 @@ def _np_ptr(a):
 
 def make_args(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host, o, *, sm_scale,
               req_to_token_stride, lse=None, qo_indptr=None, qo_indptr_host=None, num_splits=0,
-              max_q_len=0, timing_events=None):
-    """Fill the C argument struct from tensors.  Returns (args, keepalive)."""
+              max_q_len=0, timing_events=None, non_causal=False, mask=None):
+    """Fill the C argument struct from tensors.  Returns (args, keepalive).
+
+    mask: None, or a uint8 / bool tensor [B, kv_len] (2-D) or [B, q_len, kv_len] (3-D) with a
+    contiguous last dimension; nonzero = visible."""
     import torch
 
     for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool), ("o", o)):
@@ -181,6 +186,13 @@ def make_args(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host, o, *, 
     a.qo_indptr_host = _np_ptr(qoh)
     a.num_splits = int(num_splits)
     a.max_q_len = int(max_q_len)
+    a.non_causal = 1 if non_causal else 0
+    if mask is not None:
+        if mask.dtype not in (torch.uint8, torch.bool) or mask.dim() not in (2, 3) or mask.stride(-1) != 1:
+            raise TypeError("mask must be a 2-D or 3-D uint8/bool tensor with a contiguous last dimension")
+        a.mask = _ptr(mask)
+        a.mask_stride_req = mask.stride(0)
+        a.mask_stride_row = mask.stride(1) if mask.dim() == 3 else 0
     ev = None
     if timing_events is not None:
         ev = (ctypes.c_void_p * len(timing_events))(*[None if e is None else e.cuda_event for e in timing_events])
@@ -202,7 +214,8 @@ def astr_plan_decode(args: PagedArgs, num_cus: int = 0) -> DecodePlan:
 
 
 def astr_paged_decode(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host, o, workspace, *,
-                      sm_scale, req_to_token_stride, lse=None, num_splits=0, stream=None, timing_events=None):
+                      sm_scale, req_to_token_stride, lse=None, num_splits=0, stream=None, timing_events=None,
+                      mask=None):
     """Paged GQA decode: q [B, Hq, D] bf16 -> o [B, Hq, D] bf16 (+ lse [B, Hq] fp32).
 
     timing_events: optional 4 HipEvent (hip_events.py): start/end stamps of the
@@ -212,7 +225,7 @@ def astr_paged_decode(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host
     lib = load_library()
     a, keep = make_args(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host, o, sm_scale=sm_scale,
                         req_to_token_stride=req_to_token_stride, lse=lse, num_splits=num_splits,
-                        timing_events=timing_events)
+                        timing_events=timing_events, mask=mask)
     ws_ptr = _ptr(workspace)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib.astr_paged_decode(ctypes.byref(a), ws_ptr, ws_bytes, _stream_handle(stream)))
@@ -221,7 +234,7 @@ def astr_paged_decode(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host
 
 def astr_paged_prefill(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host, qo_indptr, qo_indptr_host,
                        o, *, sm_scale, req_to_token_stride, lse=None, max_q_len=0, stream=None,
-                       timing_events=None):
+                       timing_events=None, non_causal=False, mask=None):
     """Ragged paged prefill: q [sum q_len, Hq, D] bf16 in qo_indptr order -> o (+ lse).
 
     timing_events: optional 2 HipEvent (hip_events.py): start/end stamps of the
@@ -231,7 +244,8 @@ def astr_paged_prefill(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_hos
     lib = load_library()
     a, keep = make_args(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host, o, sm_scale=sm_scale,
                         req_to_token_stride=req_to_token_stride, lse=lse, qo_indptr=qo_indptr,
-                        qo_indptr_host=qo_indptr_host, max_q_len=max_q_len, timing_events=timing_events)
+                        qo_indptr_host=qo_indptr_host, max_q_len=max_q_len, timing_events=timing_events,
+                        non_causal=non_causal, mask=mask)
     _check(lib.astr_paged_prefill(ctypes.byref(a), None, 0, _stream_handle(stream)))
     del keep
 
@@ -308,7 +322,7 @@ def astr_kv_append(k_new, v_new, k_pool, v_pool, req_to_token, kv_indptr, kv_ind
 
 def astr_paged_decode_append(q, k_new, v_new, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host, o,
                              workspace, *, sm_scale, req_to_token_stride, lse=None, num_splits=0, stream=None,
-                             timing_events=None):
+                             timing_events=None, mask=None):
     """Fused KV append + paged decode: writes k_new / v_new [B, Hkv, D] (request b's new token, its last
     position) into the pools and decodes q [B, Hq, D] -> o (+ lse), bit-identical to astr_kv_append
     followed by astr_paged_decode.  timing_events as astr_paged_decode."""
@@ -320,7 +334,7 @@ def astr_paged_decode_append(q, k_new, v_new, k_pool, v_pool, req_to_token, kv_i
     lib = load_library()
     a, keep = make_args(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host, o, sm_scale=sm_scale,
                         req_to_token_stride=req_to_token_stride, lse=lse, num_splits=num_splits,
-                        timing_events=timing_events)
+                        timing_events=timing_events, mask=mask)
     nkv = make_new_kv(k_new, v_new)
     ws_ptr = _ptr(workspace)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0

@@ -139,6 +139,34 @@ int validate_common(const astr_paged_args* a, bool prefill, int64_t* total_keys)
   return ASTR_OK;
 }
 
+// The causal switch and the optional mask: alignment, strides, and rows long
+// enough for max_len keys and max_rows query rows per request.
+int validate_mask(const astr_paged_args* a, int64_t max_len, int64_t max_rows) {
+  if (a->non_causal != 0 && a->non_causal != 1) return fail(ASTR_ERR_INVALID_ARG, "non_causal must be 0 or 1");
+  if (a->mask == nullptr) return ASTR_OK;
+  if ((reinterpret_cast<uintptr_t>(a->mask) & 3u) != 0 || a->mask_stride_req % 4 != 0 || a->mask_stride_row % 4 != 0)
+    return fail(ASTR_ERR_INVALID_ARG, "the mask pointer and its strides must be multiples of 4 bytes");
+  if (a->mask_stride_req < 0 || a->mask_stride_row < 0 || a->mask_stride_req > INT32_MAX)
+    return fail(ASTR_ERR_INVALID_ARG, "mask strides must be in [0, 2^31)");
+  const int64_t row_len = a->mask_stride_row == 0 ? a->mask_stride_req : a->mask_stride_row;
+  if (row_len < max_len)
+    return fail(ASTR_ERR_INVALID_ARG, "mask rows hold %lld entries but a request has %lld keys", (long long)row_len,
+                (long long)max_len);
+  if (a->mask_stride_row > 0 && a->mask_stride_req < max_rows * a->mask_stride_row)
+    return fail(ASTR_ERR_INVALID_ARG, "mask_stride_req %lld is smaller than %lld query rows of %lld bytes",
+                (long long)a->mask_stride_req, (long long)max_rows, (long long)a->mask_stride_row);
+  return ASTR_OK;
+}
+
+int64_t max_seq_len(const astr_paged_args* a) {
+  int64_t m = 0;
+  for (int b = 0; b < a->batch; ++b) {
+    const int64_t L = (int64_t)a->kv_indptr_host[b + 1] - a->kv_indptr_host[b];
+    if (L > m) m = L;
+  }
+  return m;
+}
+
 // Bytes from a kv head's base to the end of that head's row in the last
 // slot: (num_slots - 1) * kv_stride_slot * 2 + head_dim * 2.  The kernels
 // take 32-bit buffer offsets when this is at most kPoolRange32 (the decode
@@ -274,6 +302,8 @@ int astr::decode_impl(const astr_paged_args* a, const astr_new_kv* nkv, void* wo
   if (a->qo_indptr != nullptr || a->qo_indptr_host != nullptr)
     return fail(ASTR_ERR_INVALID_ARG, "decode takes no qo_indptr (one query row per request)");
   if (a->batch == 0) return ok();
+  st = validate_mask(a, max_seq_len(a), 1);
+  if (st != ASTR_OK) return st;
   int num_cus = 0;
   if (a->num_splits == 0) {
     st = device_cu_count(&num_cus);
@@ -324,6 +354,8 @@ int astr::decode_impl(const astr_paged_args* a, const astr_new_kv* nkv, void* wo
   p.new_stride_tok = nkv != nullptr ? nkv->stride_tok : 0;
   p.new_stride_head = nkv != nullptr ? nkv->stride_head : 0;
   p.num_slots = a->num_slots;
+  p.mask = a->mask;
+  p.mask_stride_req = a->mask_stride_req;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = astr::launch_decode_split(p, s, timing_pair(a->timing_events, 0));
@@ -439,6 +471,8 @@ int astr_paged_prefill(const astr_paged_args* a, void* workspace, size_t workspa
                   (long long)L);
     if (ql > max_q) max_q = (int32_t)ql;
   }
+  st = validate_mask(a, max_seq_len(a), max_q);
+  if (st != ASTR_OK) return st;
   if (a->max_q_len > 0) {
     if (max_q > a->max_q_len)
       return fail(ASTR_ERR_INVALID_ARG, "a q_len of %d exceeds max_q_len %d", max_q, a->max_q_len);
@@ -469,6 +503,10 @@ int astr_paged_prefill(const astr_paged_args* a, void* workspace, size_t workspa
   p.kv_indptr = a->kv_indptr;
   p.qo_indptr = a->qo_indptr;
   p.max_q_len = max_q;
+  p.non_causal = a->non_causal != 0;
+  p.mask = a->mask;
+  p.mask_stride_req = a->mask_stride_req;
+  p.mask_stride_row = a->mask_stride_row;
   const int64_t range = pool_range_bytes(a);
   p.off32 = range <= kPoolRange32 && a->num_slots <= (int64_t(1) << 24) && a->kv_stride_slot * 2 < (int64_t(1) << 24);
   p.pool_range = p.off32 ? (uint32_t)range : 0u;

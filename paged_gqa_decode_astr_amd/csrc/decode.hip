@@ -96,6 +96,7 @@ template <int D>
 struct Tile {
   uint4 k[Shape<D>::kSteps];
   uint4 v[Shape<D>::kSteps];
+  uint64_t vis;   // MASK: bit j set when key j of the tile is not hidden by the mask (wavefront-uniform)
 };
 
 // Pool rows are addressed from a per-kv-head base (wavefront-uniform, so it
@@ -218,7 +219,7 @@ __device__ __forceinline__ void advance(Cursor& c, const PieceTable& pt, int wv)
   settle(c, pt, wv);
 }
 
-template <int D, int G, bool OFF32, bool APPEND>
+template <int D, int G, bool OFF32, bool APPEND, bool MASK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void decode_split_kernel(const DecodeLaunch p) {
   using S = Shape<D>;
   constexpr int NS = S::kSteps;
@@ -353,6 +354,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       if constexpr (OFF32) return t < t_end ? id : -1;
       return id;
     };
+    // MASK: the mask byte of this lane's key at cursor cu (read for the
+    // clamped key, like the slot id, so it stays inside the request's row).
+    auto mask_at = [&](const Cursor& cu) -> int {
+      if constexpr (!MASK) return 1;
+      const int j = min(cu.j, pt.n - 1);
+      const int t_end = pt.t_end(j);
+      const int t = min((cu.j < pt.n ? cu.t : t_end) + l16, t_end - 1);
+      return p.mask[(int64_t)(pt.b0 + j) * p.mask_stride_req + t];
+    };
     // q rows of pieces [j0, j0 + nb) -> sm_q[0 .. nb).  The caller brackets
     // this with barriers.
     auto stage_q = [&](int j0, int nb) {
@@ -397,10 +407,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     advance(c3, pt, wv);
     int iA = id_at(c0);
     int iB = id_at(c1);
+    int mA = mask_at(c0);
+    int mB = mask_at(c1);
     Tile<D> A, Bt;
     load_tile<D, OFF32>(A, pv, iA, lane);
+    if constexpr (MASK) A.vis = __builtin_amdgcn_ballot_w64(mA != 0);
     iA = id_at(c2);
+    mA = mask_at(c2);
     load_tile<D, OFF32>(Bt, pv, iB, lane);
+    if constexpr (MASK) Bt.vis = __builtin_amdgcn_ballot_w64(mB != 0);
     __syncthreads();
 
     float mref = -INFINITY, mx = -INFINITY, lsum = 0.f;
@@ -423,7 +438,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       bool raise = false;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        sc[r] = (c0.t + 4 * kb + r < t_end) ? st[r] * qscale : -INFINITY;
+        bool vis = c0.t + 4 * kb + r < t_end;
+        if constexpr (MASK) vis = vis && ((X.vis >> (4 * kb + r)) & 1);
+        sc[r] = vis ? st[r] * qscale : -INFINITY;
         tmax = fmaxf(tmax, sc[r]);
         raise |= sc[r] > mref + kTau;
       }
@@ -441,7 +458,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       bf16x4 phi, plo;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float pr = __builtin_amdgcn_exp2f(sc[r] - mref);
+        // MASK: a tile can start a piece with every key hidden (mref still
+        // -inf); hidden keys weigh exactly 0.
+        const float pr = (MASK && sc[r] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sc[r] - mref);
         lsum += pr;
         phi[r] = (__bf16)pr;
         plo[r] = (__bf16)(pr - (float)phi[r]);
@@ -458,10 +477,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     };
     // One pipeline step: X holds tile c0, the other buffer holds c1 (in
     // flight), iX holds the id of c2; iY is free and receives the id of c3.
-    auto step = [&](Tile<D>& X, int& iX, int& iY) {
+    auto step = [&](Tile<D>& X, int& iX, int& iY, int& mX, int& mY) {
       compute(X);
       iY = id_at(c3);
+      mY = mask_at(c3);
       load_tile<D, OFF32>(X, pv, iX, lane);
+      if constexpr (MASK) X.vis = __builtin_amdgcn_ballot_w64(mX != 0);
       c0 = c1;
       c1 = c2;
       c2 = c3;
@@ -486,8 +507,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
       t_end = pt.t_end(j);
       while (c0.j == j) {
-        step(A, iA, iB);
-        step(Bt, iB, iA);
+        step(A, iA, iB, mA, mB);
+        step(Bt, iB, iA, mB, mA);
       }
       if (is_short) {
         // The owner writes the partial: o = acc / l, and (m, l) against the
@@ -610,12 +631,16 @@ __global__ __launch_bounds__(kCombineGroupThreads * kMaxCombineGroups) void deco
 #pragma unroll
     for (int i = 0; i < kBatch; ++i)
       if (i0 + i * ngrp < n) Mb = fmaxf(Mb, m[i]);
-    const float sc = expf(M - Mb);   // M == -inf on the first batch: scales zeros
+    // M == -inf before the first piece with a visible key: num and den are 0
+    // and stay so (no 0 * inf).
+    const float sc = M == Mb ? 1.f : expf(M - Mb);
     den *= sc;
     num.x *= sc; num.y *= sc; num.z *= sc; num.w *= sc;
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
-      if (i0 + i * ngrp >= n) continue;
+      // A piece whose keys are all hidden by the mask has m = -inf and no
+      // defined o or l: it adds nothing.
+      if (i0 + i * ngrp >= n || m[i] == -INFINITY) continue;
       const float wgt = l[i] * expf(m[i] - Mb);
       den += wgt;
       num.x = fmaf(wgt, o[i].x, num.x);
@@ -637,7 +662,7 @@ __global__ __launch_bounds__(kCombineGroupThreads * kMaxCombineGroups) void deco
       const float mk = s_m[k][t];
       if (mk == -INFINITY) continue;   // group had no piece
       const float Mn = fmaxf(M, mk);
-      const float a = expf(M - Mn), c = expf(mk - Mn);   // group 0 always holds piece 0: M is finite
+      const float a = M == -INFINITY ? 0.f : expf(M - Mn), c = expf(mk - Mn);   // M = -inf: group 0 saw no visible key
       const float4 nk = s_num[k][t];
       den = den * a + s_den[k][t] * c;
       num.x = num.x * a + nk.x * c;
@@ -648,22 +673,28 @@ __global__ __launch_bounds__(kCombineGroupThreads * kMaxCombineGroups) void deco
     }
   }
   if (!live) return;
-  const float inv = 1.f / den;
+  // No visible key in the whole request (possible only with a mask): O = 0, lse = -inf.
+  const float inv = den > 0.f ? 1.f / den : 0.f;
   const uint32_t w0 = (uint32_t)f32_to_bf16_rne(num.x * inv) | ((uint32_t)f32_to_bf16_rne(num.y * inv) << 16);
   const uint32_t w1 = (uint32_t)f32_to_bf16_rne(num.z * inv) | ((uint32_t)f32_to_bf16_rne(num.w * inv) << 16);
   *reinterpret_cast<uint2*>(p.o + (int64_t)b * p.o_stride_tok + (int64_t)h * p.o_stride_head + d4) = make_uint2(w0, w1);
-  if (p.lse != nullptr && d4 == 0) p.lse[(int64_t)b * p.lse_stride_tok + h] = M + logf(den);
+  if (p.lse != nullptr && d4 == 0) p.lse[(int64_t)b * p.lse_stride_tok + h] = den > 0.f ? M + logf(den) : -INFINITY;
 }
 
 template <int D, int G>
 hipError_t launch_split_t(const DecodeLaunch& p, hipStream_t s, const Timing& t) {
   const dim3 grid(p.num_splits, p.num_kv_heads, 1);
-  if (p.k_new != nullptr) {
-    if (p.off32) return launch_kernel(decode_split_kernel<D, G, true, true>, grid, dim3(kThreads), s, t, p);
-    return launch_kernel(decode_split_kernel<D, G, false, true>, grid, dim3(kThreads), s, t, p);
+  const int variant = (p.off32 ? 4 : 0) + (p.k_new != nullptr ? 2 : 0) + (p.mask != nullptr ? 1 : 0);
+  switch (variant) {
+    case 0: return launch_kernel(decode_split_kernel<D, G, false, false, false>, grid, dim3(kThreads), s, t, p);
+    case 1: return launch_kernel(decode_split_kernel<D, G, false, false, true>, grid, dim3(kThreads), s, t, p);
+    case 2: return launch_kernel(decode_split_kernel<D, G, false, true, false>, grid, dim3(kThreads), s, t, p);
+    case 3: return launch_kernel(decode_split_kernel<D, G, false, true, true>, grid, dim3(kThreads), s, t, p);
+    case 4: return launch_kernel(decode_split_kernel<D, G, true, false, false>, grid, dim3(kThreads), s, t, p);
+    case 5: return launch_kernel(decode_split_kernel<D, G, true, false, true>, grid, dim3(kThreads), s, t, p);
+    case 6: return launch_kernel(decode_split_kernel<D, G, true, true, false>, grid, dim3(kThreads), s, t, p);
+    default: return launch_kernel(decode_split_kernel<D, G, true, true, true>, grid, dim3(kThreads), s, t, p);
   }
-  if (p.off32) return launch_kernel(decode_split_kernel<D, G, true, false>, grid, dim3(kThreads), s, t, p);
-  return launch_kernel(decode_split_kernel<D, G, false, false>, grid, dim3(kThreads), s, t, p);
 }
 
 template <int D, int G>

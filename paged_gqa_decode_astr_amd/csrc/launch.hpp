@@ -35,6 +35,10 @@ struct DecodeLaunch {
   const uint16_t* v_new;
   int64_t new_stride_tok, new_stride_head;
   int64_t num_slots;
+  // Optional uint8 mask (row 0 of each request's block): key t of request b
+  // is hidden when mask[b * mask_stride_req + t] == 0.
+  const uint8_t* mask;
+  int64_t mask_stride_req;
 };
 
 // KV append: n_b new tokens per request (1 when qo_indptr is null), written
@@ -71,6 +75,11 @@ struct PrefillLaunch {
   const int32_t* kv_indptr;
   const int32_t* qo_indptr;
   int32_t max_q_len;     // grid covers query positions [0, max_q_len)
+  bool non_causal;       // every row sees all L_b keys
+  // Optional uint8 mask: key t hidden from row i of request b when
+  // mask[b * mask_stride_req + i * mask_stride_row + t] == 0 (4-byte aligned).
+  const uint8_t* mask;
+  int64_t mask_stride_req, mask_stride_row;
   bool off32;            // 32-bit buffer offsets: pool rows of a kv head within pool_range bytes, slot ids < 2^24
   uint32_t pool_range;   // off32: (num_slots - 1) * kv_stride_slot * 2 + head_dim * 2
 };

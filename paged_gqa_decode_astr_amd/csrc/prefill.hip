@@ -70,7 +70,7 @@ struct PShape {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int D, int G, bool OFF32>
+template <int D, int G, bool OFF32, bool MASK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(const PrefillLaunch p) {
   using S = PShape<D>;
   constexpr int BQ = kRows / G;   // query positions per work group
@@ -107,7 +107,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int L = p.kv_indptr[b + 1] - kv0;
   const int cofs = L - qb;              // absolute position of query row 0
   const int npos = min(BQ, qb - p0);    // valid positions in this tile
-  const int kv_end = cofs + p0 + npos;  // keys [0, kv_end) are visible to some row
+  // Keys [0, kv_end) are visible to some row (all L keys when non-causal).
+  const int kv_end = p.non_causal ? L : cofs + p0 + npos;
   const int ntiles = (kv_end + KT - 1) / KT;
   const int32_t* ids = p.req_to_token + (p.req_to_token_stride > 0 ? (int64_t)b * p.req_to_token_stride : (int64_t)kv0);
 
@@ -189,7 +190,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int R = 32 * wv + 16 * rb + l16;
     const int posl = R / G;
     const int head = g * G + R % G;
-    lim[rb] = cofs + p0 + posl;  // last key this row may see
+    lim[rb] = p.non_causal ? L - 1 : cofs + p0 + posl;  // last key this row may see
     const bool ok = posl < npos;
 #pragma unroll
     for (int ks = 0; ks < NS; ++ks) {
@@ -198,8 +199,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       qop[rb][ks] = __builtin_bit_cast(bf16x8, v);
     }
   }
+  // MASK: lane (l16, kb) needs, for each row block rb, the mask bytes of its
+  // row (query p0 + (32 wv + 16 rb + l16) / G of the request) at keys
+  // t0 + 16 tb + 4 kb .. +3:
+  // one dword per (rb, tb), loaded one tile ahead through a buffer resource
+  // over the request's mask block, whose range check returns 0 (hidden) for
+  // anything past it.  A 2-D mask has row stride 0.
+  [[maybe_unused]] uint32_t mcur[2][4], mnext[2][4];
+  [[maybe_unused]] uint32_t mrow[2];
+  [[maybe_unused]] __amdgpu_buffer_rsrc_t mrs;
+  auto load_mask = [&](int t0, uint32_t (&dst)[2][4]) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+        dst[rb][tb] = __builtin_amdgcn_raw_buffer_load_b32(mrs, mrow[rb] + (uint32_t)(t0 + 16 * tb + 4 * kb), 0, 0);
+  };
+  if constexpr (MASK) {
+    mrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.mask + (int64_t)b * p.mask_stride_req), (short)0,
+                                            (int)p.mask_stride_req, 0x00020000);
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) mrow[rb] = (uint32_t)((p0 + (32 * wv + 16 * rb + l16) / G) * p.mask_stride_row);
+    load_mask(0, mcur);
+  }
   const float qk_scale = p.sm_scale * kLog2e;
-  const int lim_min = cofs + p0;   // smallest row limit of the work group
+  const int lim_min = p.non_causal ? L - 1 : cofs + p0;   // smallest row limit of the work group
   f32x4 acc[2][NB];
   f32x4 lacc[2];     // row sums of the weights (all four entries of a lane equal)
   float mref[2];
@@ -225,6 +249,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       if (more) {
         if constexpr (decltype(stage)::value == 0) gather(sK1, sV1); else gather(sK0, sV0);
         load_ids(t0 + 2 * KT);
+        if constexpr (MASK) load_mask(t0 + KT, mnext);
       }
       const uint16_t* kt = decltype(stage)::value == 0 ? sK0 : sK1;
       const uint16_t* vt = decltype(stage)::value == 0 ? sV0 : sV1;
@@ -257,7 +282,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         }
       }
 
-      // Causal mask (only tiles that reach past the first row's limit need it).
+      // Causal mask (only tiles that reach past the first row's limit need
+      // it), and the boolean mask (every tile of a MASK work group).
       if constexpr (decltype(masked)::value) {
   #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
@@ -265,8 +291,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   #pragma unroll
           for (int tb = 0; tb < 4; ++tb)
   #pragma unroll
-            for (int q = 0; q < 4; ++q)
-              if (16 * tb + q > thr) st[rb][tb][q] = -INFINITY;
+            for (int q = 0; q < 4; ++q) {
+              bool hide = 16 * tb + q > thr;
+              if constexpr (MASK) hide = hide || ((mcur[rb][tb] >> (8 * q)) & 0xffu) == 0u;
+              if (hide) st[rb][tb][q] = -INFINITY;
+            }
         }
       }
       bf16x8 pop[2][2];
@@ -292,7 +321,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
           for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, st[rb][i / 4][i % 4]);
           tmax = xor_max<16, kWave>(tmax) * qk_scale;
           const float mnew = fmaxf(mref[rb], tmax);
-          const float alpha = exp2f(mref[rb] - mnew);     // mref == -inf on the first tile: scales zeros
+          // mref == -inf before the row's first visible key: alpha is 0 (or,
+          // MASK, 1 while the row still has none: exp2(-inf - -inf) would be
+          // NaN, and NaN * 0 is not 0).
+          float alpha = exp2f(mref[rb] - mnew);
+          if constexpr (MASK) alpha = mnew == -INFINITY ? 1.f : alpha;
           mref[rb] = mnew;
           lacc[rb] *= alpha;
   #pragma unroll
@@ -342,6 +375,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       }
 
       stage_ready();   // the next stage is loaded; this one may be overwritten
+      if constexpr (MASK) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int tb = 0; tb < 4; ++tb) mcur[rb][tb] = mnext[rb][tb];
+      }
     }
   };
   using S0 = std::integral_constant<int, 0>;
@@ -356,7 +395,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
     if (it < it_end) tile(masked, S0{}, it);
   };
-  const int it_plain = min(ntiles, (lim_min + 1) / KT);
+  const int it_plain = MASK ? 0 : min(ntiles, (lim_min + 1) / KT);
   run_tiles(std::false_type{}, 0, it_plain);
   run_tiles(std::true_type{}, it_plain, ntiles);
 
@@ -369,7 +408,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     if (posl >= npos) continue;
     const int row = q0 + p0 + posl;
     const int head = g * G + R % G;
-    const float inv = 1.f / ltot;
+    // A row with no visible key (only possible with a mask) is written as
+    // zeros with lse = -inf.
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     uint16_t* orow = p.o + (int64_t)row * p.o_stride_tok + (int64_t)head * p.o_stride_head;
 #pragma unroll
     for (int db = 0; db < NB; ++db) {
@@ -377,7 +418,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       const uint32_t w1 = (uint32_t)f32_to_bf16_rne(acc[rb][db][2] * inv) | ((uint32_t)f32_to_bf16_rne(acc[rb][db][3] * inv) << 16);
       *reinterpret_cast<uint2*>(orow + 16 * db + 4 * kb) = make_uint2(w0, w1);
     }
-    if (p.lse != nullptr && kb == 0) p.lse[(int64_t)row * p.lse_stride_tok + head] = (mref[rb] + log2f(ltot)) * kLn2;
+    if (p.lse != nullptr && kb == 0)
+      p.lse[(int64_t)row * p.lse_stride_tok + head] = ltot > 0.f ? (mref[rb] + log2f(ltot)) * kLn2 : -INFINITY;
   }
 }
 
@@ -388,8 +430,13 @@ hipError_t launch_t(const PrefillLaunch& p, hipStream_t s, const Timing& t) {
   const int64_t groups = (int64_t)p.num_kv_heads * p.batch;
   const int64_t blocks = kXcds * ((groups + kXcds - 1) / kXcds) * nq;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  if (p.off32) return launch_kernel(prefill_kernel<D, G, true>, dim3((unsigned)blocks, 1, 1), dim3(kThreads), s, t, p);
-  return launch_kernel(prefill_kernel<D, G, false>, dim3((unsigned)blocks, 1, 1), dim3(kThreads), s, t, p);
+  const dim3 grid((unsigned)blocks, 1, 1);
+  if (p.mask != nullptr) {
+    if (p.off32) return launch_kernel(prefill_kernel<D, G, true, true>, grid, dim3(kThreads), s, t, p);
+    return launch_kernel(prefill_kernel<D, G, false, true>, grid, dim3(kThreads), s, t, p);
+  }
+  if (p.off32) return launch_kernel(prefill_kernel<D, G, true, false>, grid, dim3(kThreads), s, t, p);
+  return launch_kernel(prefill_kernel<D, G, false, false>, grid, dim3(kThreads), s, t, p);
 }
 
 }  // namespace

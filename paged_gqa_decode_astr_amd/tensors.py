@@ -43,7 +43,8 @@ def decode_workspace(batch: int, num_qo_heads: int, head_dim: int, device="cuda"
     return torch.full((n,), fill, dtype=torch.float32, device=device)
 
 
-def run_decode(dev: dict, o=None, lse=None, workspace=None, num_splits=0, stream=None, timing_events=None):
+def run_decode(dev: dict, o=None, lse=None, workspace=None, num_splits=0, stream=None, timing_events=None,
+               mask=None):
     q = dev["q"]
     if o is None:
         o = torch.empty_like(q)
@@ -53,7 +54,7 @@ def run_decode(dev: dict, o=None, lse=None, workspace=None, num_splits=0, stream
     _lib.astr_paged_decode(q, dev["k_pool"], dev["v_pool"], dev["req_to_token"], dev["kv_indptr"],
                            dev["kv_indptr_host"], o, workspace, sm_scale=dev["sm_scale"],
                            req_to_token_stride=dev["req_to_token_stride"], lse=lse, num_splits=num_splits,
-                           stream=stream, timing_events=timing_events)
+                           stream=stream, timing_events=timing_events, mask=mask)
     return o
 
 
@@ -65,7 +66,8 @@ def run_append(dev: dict, stream=None, timing_events=None, max_q_len=0):
                         stream=stream, timing_events=timing_events)
 
 
-def run_decode_append(dev: dict, o=None, lse=None, workspace=None, num_splits=0, stream=None, timing_events=None):
+def run_decode_append(dev: dict, o=None, lse=None, workspace=None, num_splits=0, stream=None, timing_events=None,
+                      mask=None):
     """Fused append of dev["k_new"] / dev["v_new"] and decode."""
     q = dev["q"]
     if o is None:
@@ -76,18 +78,20 @@ def run_decode_append(dev: dict, o=None, lse=None, workspace=None, num_splits=0,
     _lib.astr_paged_decode_append(q, dev["k_new"], dev["v_new"], dev["k_pool"], dev["v_pool"], dev["req_to_token"],
                                   dev["kv_indptr"], dev["kv_indptr_host"], o, workspace, sm_scale=dev["sm_scale"],
                                   req_to_token_stride=dev["req_to_token_stride"], lse=lse, num_splits=num_splits,
-                                  stream=stream, timing_events=timing_events)
+                                  stream=stream, timing_events=timing_events, mask=mask)
     return o
 
 
-def run_prefill(dev: dict, o=None, lse=None, max_q_len=0, stream=None, timing_events=None):
+def run_prefill(dev: dict, o=None, lse=None, max_q_len=0, stream=None, timing_events=None, non_causal=False,
+                mask=None):
     q = dev["q"]
     if o is None:
         o = torch.empty_like(q)
     _lib.astr_paged_prefill(q, dev["k_pool"], dev["v_pool"], dev["req_to_token"], dev["kv_indptr"],
                             dev["kv_indptr_host"], dev["qo_indptr"], dev["qo_indptr_host"], o,
                             sm_scale=dev["sm_scale"], req_to_token_stride=dev["req_to_token_stride"], lse=lse,
-                            max_q_len=max_q_len, stream=stream, timing_events=timing_events)
+                            max_q_len=max_q_len, stream=stream, timing_events=timing_events,
+                            non_causal=non_causal, mask=mask)
     return o
 
 

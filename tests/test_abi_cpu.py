@@ -287,3 +287,31 @@ def test_graph_create_rejects_bad_arguments():
     assert lib.astr_decode_graph_create(arr, None, 2, FAKE, 1 << 30, FAKE, None) == _lib.ASTR_ERR_INVALID_ARG
     assert lib.astr_decode_graph_launch(None, None) == _lib.ASTR_ERR_INVALID_ARG
     assert lib.astr_decode_graph_destroy(None) == _lib.ASTR_OK
+
+
+# --------------------------------------------------------------------------- causal switch and mask validation
+
+@pytest.mark.parametrize("setup,needle", [
+    (lambda a: setattr(a, "non_causal", 2), "non_causal"),
+    (lambda a: (setattr(a, "mask", FAKE + 2), setattr(a, "mask_stride_req", 8)), "multiples of 4"),
+    (lambda a: (setattr(a, "mask", FAKE), setattr(a, "mask_stride_req", 6)), "multiples of 4"),
+    (lambda a: (setattr(a, "mask", FAKE), setattr(a, "mask_stride_req", 4)), "mask rows hold 4"),
+    (lambda a: (setattr(a, "mask", FAKE), setattr(a, "mask_stride_req", 8), setattr(a, "mask_stride_row", 4)),
+     "mask rows hold 4"),
+    (lambda a: (setattr(a, "mask", FAKE), setattr(a, "mask_stride_req", -4)), "mask strides"),
+    (lambda a: (setattr(a, "mask", FAKE), setattr(a, "mask_stride_req", 1 << 32)), "mask strides"),
+])
+def test_decode_rejects_bad_mask(setup, needle):
+    a, keep = _valid_decode_args((0, 3, 9))   # seq_lens 3 and 6
+    setup(a)
+    assert _call_decode(a) == _lib.ASTR_ERR_INVALID_ARG
+    assert needle in _lib.astr_last_error()
+
+
+def test_prefill_mask_needs_rows_for_every_query():
+    a, keep = _valid_prefill_args(qo=(0, 2, 3))      # q_lens 2 and 1, seq_lens 3 and 4
+    a.mask = FAKE
+    a.mask_stride_row = 4
+    a.mask_stride_req = 4                              # one row, but request 0 has two query rows
+    assert _call_prefill(a) == _lib.ASTR_ERR_INVALID_ARG
+    assert "query rows" in _lib.astr_last_error()
