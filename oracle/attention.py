@@ -70,15 +70,27 @@ def f64_to_bf16_bits(x) -> np.ndarray:
     return out
 
 
-def request_slots(req_to_token, req_to_token_stride, kv_indptr, b) -> np.ndarray:
+def request_slots(req_to_token, req_to_token_stride, kv_indptr, b, page_size=1) -> np.ndarray:
     """Pool slots of request b's positions 0..L_b-1.
 
     Row base is b * stride for a 2-D table, or kv_indptr[b] for a flat table
-    (stride 0).  Page size is one: position t maps to exactly one slot.
+    (stride 0).  With page size one, entry t of the row is position t's slot.
+    With page size P > 1 (the pages name a paged allocation strategy beside
+    the page-size-one table; reading taken: a 2-D table whose entries are page
+    ids, P token slots per page), position t lives in slot
+    row[t // P] * P + t % P.
     """
     L = int(kv_indptr[b + 1]) - int(kv_indptr[b])
-    base = b * int(req_to_token_stride) if req_to_token_stride > 0 else int(kv_indptr[b])
-    return np.asarray(req_to_token[base: base + L], dtype=np.int64)
+    P = int(page_size)
+    if P == 1:
+        base = b * int(req_to_token_stride) if req_to_token_stride > 0 else int(kv_indptr[b])
+        return np.asarray(req_to_token[base: base + L], dtype=np.int64)
+    if req_to_token_stride <= 0:
+        raise ValueError("a page size above one needs a 2-D page table (row stride > 0)")
+    row = np.asarray(req_to_token[b * int(req_to_token_stride): b * int(req_to_token_stride) + (L + P - 1) // P],
+                     dtype=np.int64)
+    t = np.arange(L)
+    return row[t // P] * P + t % P
 
 
 def attention_over_range(qf, kf, vf, sigma, visible):
@@ -101,7 +113,7 @@ def attention_over_range(qf, kf, vf, sigma, visible):
 
 
 def paged_attention(q_bits, k_pool_bits, v_pool_bits, req_to_token, req_to_token_stride,
-                    kv_indptr, sm_scale, qo_indptr=None, non_causal=False, mask=None):
+                    kv_indptr, sm_scale, qo_indptr=None, non_causal=False, mask=None, page_size=1):
     """Reference paged GQA attention.
 
     q_bits: [rows, Hq, D] bf16 bits; rows = B for decode (qo_indptr None) or
@@ -114,6 +126,7 @@ def paged_attention(q_bits, k_pool_bits, v_pool_bits, req_to_token, req_to_token
     (3-D) is zero, on top of the causal rule.
     Returns (o [rows, Hq, D] float64, lse [rows, Hq] float64 natural log);
     rows with no visible key get o = 0 and lse = -inf.
+    page_size: token slots per page of req_to_token's entries (see request_slots).
     Requires 1 <= q_len_b <= seq_len_b for every request.
     """
     q_bits = np.asarray(q_bits)
@@ -137,7 +150,7 @@ def paged_attention(q_bits, k_pool_bits, v_pool_bits, req_to_token, req_to_token
         if not (1 <= qb <= L):
             raise ValueError(f"request {b}: need 1 <= q_len ({qb}) <= seq_len ({L})")
         c = L - qb  # absolute position of the first query row
-        slots = request_slots(req_to_token, req_to_token_stride, kv_indptr, b)
+        slots = request_slots(req_to_token, req_to_token_stride, kv_indptr, b, page_size)
         K = bf16_bits_to_f64(k_pool_bits[slots])   # [L, Hkv, D]
         V = bf16_bits_to_f64(v_pool_bits[slots])
         Q = bf16_bits_to_f64(q_bits[row0: row0 + qb])  # [qb, Hq, D]

@@ -35,7 +35,7 @@ import numpy as np
 from .attention import request_slots
 
 
-def new_token_slots(req_to_token, req_to_token_stride, kv_indptr, qo_indptr=None):
+def new_token_slots(req_to_token, req_to_token_stride, kv_indptr, qo_indptr=None, page_size=1):
     """Pool slot of every new token, in flat new-row order ([sum n_b] int64)."""
     kv_indptr = np.asarray(kv_indptr, dtype=np.int64)
     B = kv_indptr.shape[0] - 1
@@ -45,7 +45,7 @@ def new_token_slots(req_to_token, req_to_token_stride, kv_indptr, qo_indptr=None
         n = 1 if qo_indptr is None else int(qo_indptr[b + 1]) - int(qo_indptr[b])
         if not (1 <= n <= L):
             raise ValueError(f"request {b}: need 1 <= new tokens ({n}) <= seq_len ({L})")
-        slots = request_slots(req_to_token, req_to_token_stride, kv_indptr, b)
+        slots = request_slots(req_to_token, req_to_token_stride, kv_indptr, b, page_size)
         for i in range(n):
             out.append(int(slots[L - n + i]))
     out = np.asarray(out, dtype=np.int64)
@@ -55,7 +55,7 @@ def new_token_slots(req_to_token, req_to_token_stride, kv_indptr, qo_indptr=None
 
 
 def kv_append(k_pool_bits, v_pool_bits, k_new_bits, v_new_bits, req_to_token, req_to_token_stride,
-              kv_indptr, qo_indptr=None):
+              kv_indptr, qo_indptr=None, page_size=1):
     """Pools after writing the new tokens' rows.
 
     k_pool_bits, v_pool_bits: [num_slots, Hkv, D] bf16 bits (not modified).
@@ -66,7 +66,7 @@ def kv_append(k_pool_bits, v_pool_bits, k_new_bits, v_new_bits, req_to_token, re
     """
     k = np.array(k_pool_bits, copy=True)
     v = np.array(v_pool_bits, copy=True)
-    slots = new_token_slots(req_to_token, req_to_token_stride, kv_indptr, qo_indptr)
+    slots = new_token_slots(req_to_token, req_to_token_stride, kv_indptr, qo_indptr, page_size)
     k_new = np.asarray(k_new_bits)
     v_new = np.asarray(v_new_bits)
     if k_new.shape[0] != slots.shape[0] or v_new.shape[0] != slots.shape[0]:

@@ -96,7 +96,7 @@ def _draw_seq_lens(cfg: Config, gen: torch.Generator) -> np.ndarray:
 
 def build_paged_inputs(seq_lens, num_qo_heads, num_kv_heads, head_dim, num_slots, seed,
                        q_lens=None, row_stride=None, peaky_keys=0, flat_table=False,
-                       poison_unused=True, new_tokens=None):
+                       poison_unused=True, new_tokens=None, page_size=1):
     """Build one batch of paged inputs.
 
     seq_lens: per-request KV length L_b.  q_lens: per-request number of query
@@ -111,6 +111,11 @@ def build_paged_inputs(seq_lens, num_qo_heads, num_kv_heads, head_dim, num_slots
     request order) instead of being stored, and their slots keep the unused
     fill; ``k_pool_full`` / ``v_pool_full`` hold the pools with every position
     stored, for comparison.
+
+    page_size: P > 1 hands out whole pages of P consecutive slots (a random
+    permutation of the num_slots / P pages, fresh pages per request) and
+    returns req_to_token as a 2-D table of page ids; ``token_slots`` then
+    lists every position's slot in flat key order.
     """
     seq_lens = np.asarray(seq_lens, dtype=np.int64)
     B = int(seq_lens.shape[0])
@@ -120,9 +125,35 @@ def build_paged_inputs(seq_lens, num_qo_heads, num_kv_heads, head_dim, num_slots
         raise ValueError(f"pool of {num_slots} slots is smaller than total length {N}")
     kv_indptr = np.zeros(B + 1, dtype=np.int32)
     kv_indptr[1:] = np.cumsum(seq_lens)
-    perm = torch.randperm(num_slots, generator=gen).numpy().astype(np.int32)
-    slots_flat = perm[:N].copy()
-    if flat_table:
+    P = int(page_size)
+    if P > 1:
+        if flat_table:
+            raise ValueError("a page size above one uses a 2-D page table")
+        npages = [(int(L) + P - 1) // P for L in seq_lens]
+        if sum(npages) * P > num_slots:
+            raise ValueError(f"pool of {num_slots} slots holds fewer than {sum(npages)} pages of {P}")
+        pages = torch.randperm(num_slots // P, generator=gen).numpy().astype(np.int32)
+        stride = int(row_stride) if row_stride is not None else max(1, max(npages) if B else 1)
+        req_to_token = np.full((B, stride), -1, dtype=np.int32)
+        slots_flat = np.empty(N, dtype=np.int32)
+        nxt = 0
+        for b in range(B):
+            mine = pages[nxt: nxt + npages[b]]
+            nxt += npages[b]
+            req_to_token[b, : npages[b]] = mine
+            # Page k of the request holds its next run of up to P positions in
+            # P consecutive slots starting at slot mine[k] * P.
+            for k in range(npages[b]):
+                lo = int(kv_indptr[b]) + k * P
+                hi = min(lo + P, int(kv_indptr[b + 1]))
+                slots_flat[lo:hi] = np.arange(int(mine[k]) * P, int(mine[k]) * P + (hi - lo))
+        req_to_token = req_to_token.reshape(-1)
+    else:
+        perm = torch.randperm(num_slots, generator=gen).numpy().astype(np.int32)
+        slots_flat = perm[:N].copy()
+    if P > 1:
+        pass   # req_to_token is the page table built above
+    elif flat_table:
         req_to_token = slots_flat.copy()
         stride = 0
     else:
@@ -184,6 +215,7 @@ def build_paged_inputs(seq_lens, num_qo_heads, num_kv_heads, head_dim, num_slots
         "seq_lens": seq_lens.astype(np.int32),
         "num_qo_heads": num_qo_heads, "num_kv_heads": num_kv_heads, "head_dim": head_dim,
         "num_slots": num_slots, "sm_scale": 1.0 / math.sqrt(head_dim),
+        "page_size": P, "token_slots": slots_flat,
     }
 
 
