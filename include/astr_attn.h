@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define ASTR_ABI_VERSION 3
+#define ASTR_ABI_VERSION 4
 
 /* Default cap on work groups per kv head in an automatic decode plan. */
 #define ASTR_DEFAULT_MAX_SPLITS 256
@@ -80,7 +80,7 @@ typedef struct astr_paged_args {
   int32_t batch;          /* B >= 0 requests; B == 0 is a no-op */
   int32_t num_qo_heads;   /* Hq >= 1 */
   int32_t num_kv_heads;   /* Hkv >= 1, Hq % Hkv == 0, Hq / Hkv in {1, 2, 4, 8} */
-  int32_t head_dim;       /* D in {64, 128} */
+  int32_t head_dim;       /* D in {32, 64, 128} */
   float sm_scale;         /* logit scale, finite and > 0, e.g. 1/sqrt(D) */
 
   /* Queries, bf16.  Decode: row b is request b's query.  Prefill: rows in flat
@@ -152,6 +152,15 @@ typedef struct astr_paged_args {
    * visible key outputs zeros and lse = -inf. */
   const uint8_t* mask;
   int64_t mask_stride_req, mask_stride_row;
+
+  /* Token slots per page of req_to_token's entries: 0 or 1 (default) -- each
+   * entry is one position's slot; P > 1 (a power of two, at most 2^16) -- a
+   * 2-D table (req_to_token_stride > 0, at least ceil(L_b / P) entries per
+   * row) of page ids, position t of request b living in slot
+   * req_to_token[b * stride + t / P] * P + t % P, so num_slots counts token
+   * slots (pages * P).  The pages call for a paged allocation strategy next to
+   * the page-size-one table; this is the reading taken for it. */
+  int32_t page_size;
 } astr_paged_args;
 
 typedef struct astr_decode_plan {

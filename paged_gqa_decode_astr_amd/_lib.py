@@ -52,6 +52,7 @@ class PagedArgs(ctypes.Structure):
         ("timing_events", ctypes.c_void_p),
         ("non_causal", ctypes.c_int32), ("mask", ctypes.c_void_p),
         ("mask_stride_req", ctypes.c_int64), ("mask_stride_row", ctypes.c_int64),
+        ("page_size", ctypes.c_int32),
     ]
 
 
@@ -141,7 +142,7 @@ def _np_ptr(a):
 
 def make_args(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host, o, *, sm_scale,
               req_to_token_stride, lse=None, qo_indptr=None, qo_indptr_host=None, num_splits=0,
-              max_q_len=0, timing_events=None, non_causal=False, mask=None):
+              max_q_len=0, timing_events=None, non_causal=False, mask=None, page_size=1):
     """Fill the C argument struct from tensors.  Returns (args, keepalive).
 
     mask: None, or a uint8 / bool tensor [B, kv_len] (2-D) or [B, q_len, kv_len] (3-D) with a
@@ -187,6 +188,7 @@ def make_args(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host, o, *, 
     a.num_splits = int(num_splits)
     a.max_q_len = int(max_q_len)
     a.non_causal = 1 if non_causal else 0
+    a.page_size = int(page_size)
     if mask is not None:
         if mask.dtype not in (torch.uint8, torch.bool) or mask.dim() not in (2, 3) or mask.stride(-1) != 1:
             raise TypeError("mask must be a 2-D or 3-D uint8/bool tensor with a contiguous last dimension")
@@ -215,7 +217,7 @@ def astr_plan_decode(args: PagedArgs, num_cus: int = 0) -> DecodePlan:
 
 def astr_paged_decode(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host, o, workspace, *,
                       sm_scale, req_to_token_stride, lse=None, num_splits=0, stream=None, timing_events=None,
-                      mask=None):
+                      mask=None, page_size=1):
     """Paged GQA decode: q [B, Hq, D] bf16 -> o [B, Hq, D] bf16 (+ lse [B, Hq] fp32).
 
     timing_events: optional 4 HipEvent (hip_events.py): start/end stamps of the
@@ -225,7 +227,7 @@ def astr_paged_decode(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host
     lib = load_library()
     a, keep = make_args(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host, o, sm_scale=sm_scale,
                         req_to_token_stride=req_to_token_stride, lse=lse, num_splits=num_splits,
-                        timing_events=timing_events, mask=mask)
+                        timing_events=timing_events, mask=mask, page_size=page_size)
     ws_ptr = _ptr(workspace)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib.astr_paged_decode(ctypes.byref(a), ws_ptr, ws_bytes, _stream_handle(stream)))
@@ -234,7 +236,7 @@ def astr_paged_decode(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host
 
 def astr_paged_prefill(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host, qo_indptr, qo_indptr_host,
                        o, *, sm_scale, req_to_token_stride, lse=None, max_q_len=0, stream=None,
-                       timing_events=None, non_causal=False, mask=None):
+                       timing_events=None, non_causal=False, mask=None, page_size=1):
     """Ragged paged prefill: q [sum q_len, Hq, D] bf16 in qo_indptr order -> o (+ lse).
 
     timing_events: optional 2 HipEvent (hip_events.py): start/end stamps of the
@@ -245,7 +247,7 @@ def astr_paged_prefill(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_hos
     a, keep = make_args(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host, o, sm_scale=sm_scale,
                         req_to_token_stride=req_to_token_stride, lse=lse, qo_indptr=qo_indptr,
                         qo_indptr_host=qo_indptr_host, max_q_len=max_q_len, timing_events=timing_events,
-                        non_causal=non_causal, mask=mask)
+                        non_causal=non_causal, mask=mask, page_size=page_size)
     _check(lib.astr_paged_prefill(ctypes.byref(a), None, 0, _stream_handle(stream)))
     del keep
 
@@ -270,7 +272,7 @@ def make_new_kv(k_new, v_new) -> NewKV:
 
 def astr_kv_append(k_new, v_new, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host, *,
                    req_to_token_stride, qo_indptr=None, qo_indptr_host=None, max_q_len=0, stream=None,
-                   timing_events=None):
+                   timing_events=None, page_size=1):
     """Write the new tokens' rows k_new / v_new [sum n_b, Hkv, D] bf16 into the pools (in place).
 
     kv_indptr counts the new tokens; n_b = 1 per request without qo_indptr (decode), else
@@ -311,6 +313,7 @@ def astr_kv_append(k_new, v_new, k_pool, v_pool, req_to_token, kv_indptr, kv_ind
     a.qo_indptr = _ptr(qo_indptr)
     a.qo_indptr_host = _np_ptr(qoh)
     a.max_q_len = int(max_q_len)
+    a.page_size = int(page_size)
     ev = None
     if timing_events is not None:
         ev = (ctypes.c_void_p * 2)(*[None if e is None else e.cuda_event for e in timing_events])
@@ -322,7 +325,7 @@ def astr_kv_append(k_new, v_new, k_pool, v_pool, req_to_token, kv_indptr, kv_ind
 
 def astr_paged_decode_append(q, k_new, v_new, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host, o,
                              workspace, *, sm_scale, req_to_token_stride, lse=None, num_splits=0, stream=None,
-                             timing_events=None, mask=None):
+                             timing_events=None, mask=None, page_size=1):
     """Fused KV append + paged decode: writes k_new / v_new [B, Hkv, D] (request b's new token, its last
     position) into the pools and decodes q [B, Hq, D] -> o (+ lse), bit-identical to astr_kv_append
     followed by astr_paged_decode.  timing_events as astr_paged_decode."""
@@ -334,7 +337,7 @@ def astr_paged_decode_append(q, k_new, v_new, k_pool, v_pool, req_to_token, kv_i
     lib = load_library()
     a, keep = make_args(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host, o, sm_scale=sm_scale,
                         req_to_token_stride=req_to_token_stride, lse=lse, num_splits=num_splits,
-                        timing_events=timing_events, mask=mask)
+                        timing_events=timing_events, mask=mask, page_size=page_size)
     nkv = make_new_kv(k_new, v_new)
     ws_ptr = _ptr(workspace)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0

@@ -83,6 +83,27 @@ int device_cu_count(int* out) {
   return ASTR_OK;
 }
 
+// Page size -> log2, or -1 when it is not 0, 1 or a power of two up to 2^16.
+int page_shift_of(int32_t page_size) {
+  if (page_size == 0 || page_size == 1) return 0;
+  for (int s = 1; s <= 16; ++s)
+    if (page_size == (1 << s)) return s;
+  return -1;
+}
+
+// The page-size rules shared by every entry point; *shift receives log2 P.
+int validate_pages(const astr_paged_args* a, int* shift) {
+  *shift = page_shift_of(a->page_size);
+  if (*shift < 0) return fail(ASTR_ERR_INVALID_ARG, "page_size must be 0, 1 or a power of two up to 65536 (got %d)",
+                              a->page_size);
+  if (*shift > 0 && a->req_to_token_stride <= 0)
+    return fail(ASTR_ERR_INVALID_ARG, "a page size above one needs a 2-D page table (req_to_token_stride > 0)");
+  return ASTR_OK;
+}
+
+// Table entries request b's row needs: L_b, or ceil(L_b / P) with pages.
+int64_t row_entries(int64_t L, int shift) { return shift == 0 ? L : ((L - 1) >> shift) + 1; }
+
 // Checks shared by decode and prefill.  Sets *total_keys = kv_indptr[B].
 int validate_common(const astr_paged_args* a, bool prefill, int64_t* total_keys) {
   if (a == nullptr) return fail(ASTR_ERR_INVALID_ARG, "args is NULL");
@@ -98,7 +119,7 @@ int validate_common(const astr_paged_args* a, bool prefill, int64_t* total_keys)
   const int group = a->num_qo_heads / a->num_kv_heads;
   const bool supported = prefill ? astr::prefill_supported(a->head_dim, group) : astr::decode_supported(a->head_dim, group);
   if (!supported)
-    return fail(ASTR_ERR_UNSUPPORTED, "no kernel for head_dim=%d and group size %d (head_dim in {64,128}, group in {1,2,4,8})",
+    return fail(ASTR_ERR_UNSUPPORTED, "no kernel for head_dim=%d and group size %d (head_dim in {32,64,128}, group in {1,2,4,8})",
                 a->head_dim, group);
   if (!(a->sm_scale > 0.f) || a->sm_scale == __builtin_inff())
     return fail(ASTR_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
@@ -126,14 +147,17 @@ int validate_common(const astr_paged_args* a, bool prefill, int64_t* total_keys)
     return fail(ASTR_ERR_INVALID_ARG, "num_slots must be in [1, 2^31] (got %lld)", (long long)a->num_slots);
   if (a->req_to_token_stride < 0) return fail(ASTR_ERR_INVALID_ARG, "req_to_token_stride must be >= 0");
 
+  int shift = 0;
+  const int pst = validate_pages(a, &shift);
+  if (pst != ASTR_OK) return pst;
   const int32_t* kv = a->kv_indptr_host;
   if (kv[0] != 0) return fail(ASTR_ERR_INVALID_ARG, "kv_indptr[0] must be 0 (got %d)", kv[0]);
   for (int b = 0; b < a->batch; ++b) {
     const int64_t L = (int64_t)kv[b + 1] - kv[b];
     if (L < 1) return fail(ASTR_ERR_INVALID_ARG, "request %d: seq_len must be >= 1 (got %lld)", b, (long long)L);
-    if (a->req_to_token_stride > 0 && L > a->req_to_token_stride)
-      return fail(ASTR_ERR_INVALID_ARG, "request %d: seq_len %lld exceeds req_to_token_stride %lld", b, (long long)L,
-                  (long long)a->req_to_token_stride);
+    if (a->req_to_token_stride > 0 && row_entries(L, shift) > a->req_to_token_stride)
+      return fail(ASTR_ERR_INVALID_ARG, "request %d: seq_len %lld needs %lld table entries, more than req_to_token_stride %lld",
+                  b, (long long)L, (long long)row_entries(L, shift), (long long)a->req_to_token_stride);
   }
   *total_keys = kv[a->batch];
   return ASTR_OK;
@@ -356,6 +380,7 @@ int astr::decode_impl(const astr_paged_args* a, const astr_new_kv* nkv, void* wo
   p.num_slots = a->num_slots;
   p.mask = a->mask;
   p.mask_stride_req = a->mask_stride_req;
+  p.page_shift = page_shift_of(a->page_size);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = astr::launch_decode_split(p, s, timing_pair(a->timing_events, 0));
@@ -401,6 +426,9 @@ int astr_kv_append(const astr_paged_args* a, const astr_new_kv* nkv, void* strea
   if (a->req_to_token_stride < 0) return fail(ASTR_ERR_INVALID_ARG, "req_to_token_stride must be >= 0");
   if ((a->qo_indptr == nullptr) != (a->qo_indptr_host == nullptr))
     return fail(ASTR_ERR_INVALID_ARG, "qo_indptr and qo_indptr_host must both be set or both be NULL");
+  int shift = 0;
+  st = validate_pages(a, &shift);
+  if (st != ASTR_OK) return st;
   const int32_t* kv = a->kv_indptr_host;
   const int32_t* qo = a->qo_indptr_host;
   if (kv[0] != 0) return fail(ASTR_ERR_INVALID_ARG, "kv_indptr[0] must be 0 (got %d)", kv[0]);
@@ -412,9 +440,9 @@ int astr_kv_append(const astr_paged_args* a, const astr_new_kv* nkv, void* strea
     if (n < 1 || n > L)
       return fail(ASTR_ERR_INVALID_ARG, "request %d: need 1 <= new tokens <= seq_len (new %lld, seq_len %lld)", b,
                   (long long)n, (long long)L);
-    if (a->req_to_token_stride > 0 && L > a->req_to_token_stride)
-      return fail(ASTR_ERR_INVALID_ARG, "request %d: seq_len %lld exceeds req_to_token_stride %lld", b, (long long)L,
-                  (long long)a->req_to_token_stride);
+    if (a->req_to_token_stride > 0 && row_entries(L, shift) > a->req_to_token_stride)
+      return fail(ASTR_ERR_INVALID_ARG, "request %d: seq_len %lld needs %lld table entries, more than req_to_token_stride %lld",
+                  b, (long long)L, (long long)row_entries(L, shift), (long long)a->req_to_token_stride);
     if (n > max_new) max_new = n;
   }
   if (a->max_q_len > 0) {
@@ -444,6 +472,7 @@ int astr_kv_append(const astr_paged_args* a, const astr_new_kv* nkv, void* strea
   p.req_to_token_stride = a->req_to_token_stride;
   p.kv_indptr = a->kv_indptr;
   p.qo_indptr = a->qo_indptr;
+  p.page_shift = shift;
   const hipError_t e = astr::launch_kv_append(p, static_cast<hipStream_t>(stream), timing_pair(a->timing_events, 0));
   if (e != hipSuccess) return fail(ASTR_ERR_HIP, "append kernel launch: %s", hipGetErrorString(e));
   return ok();
@@ -507,6 +536,7 @@ int astr_paged_prefill(const astr_paged_args* a, void* workspace, size_t workspa
   p.mask = a->mask;
   p.mask_stride_req = a->mask_stride_req;
   p.mask_stride_row = a->mask_stride_row;
+  p.page_shift = page_shift_of(a->page_size);
   const int64_t range = pool_range_bytes(a);
   p.off32 = range <= kPoolRange32 && a->num_slots <= (int64_t(1) << 24) && a->kv_stride_slot * 2 < (int64_t(1) << 24);
   p.pool_range = p.off32 ? (uint32_t)range : 0u;

@@ -41,7 +41,9 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(const AppendL
   const int64_t n = p.qo_indptr != nullptr ? (int64_t)p.qo_indptr[b + 1] - row0 : 1;
   if (i >= n) return;
   const int64_t rowb = p.req_to_token_stride > 0 ? (int64_t)b * p.req_to_token_stride : kv0;
-  const int32_t slot = p.req_to_token[rowb + L - n + i];
+  const int64_t pos = L - n + i;
+  const int32_t slot = (p.req_to_token[rowb + (pos >> p.page_shift)] << p.page_shift) +
+                       (int32_t)(pos & ((1 << p.page_shift) - 1));
   if (slot < 0 || (int64_t)slot >= p.num_slots) return;   // outside the pool: nothing is written
   const int64_t src = (row0 + i) * p.new_stride_tok + (int64_t)g * p.new_stride_head + 8 * dc;
   const int64_t dst = (int64_t)slot * p.kv_stride_slot + (int64_t)g * p.kv_stride_head + 8 * dc;

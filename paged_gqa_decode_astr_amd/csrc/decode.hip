@@ -294,7 +294,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     const int64_t kb0 = kvp(b);
     const int64_t L = kvp(b + 1) - kb0;
     const int32_t* row = p.req_to_token + (p.req_to_token_stride > 0 ? (int64_t)b * p.req_to_token_stride : kb0);
-    slot = row[L - 1];
+    slot = (row[(L - 1) >> p.page_shift] << p.page_shift) + (int)((L - 1) & ((1 << p.page_shift) - 1));
     val = load16((((t / (D / 8)) & 1) ? p.v_new : p.k_new) + (int64_t)b * p.new_stride_tok +
                  (int64_t)g * p.new_stride_head + 8 * (t % (D / 8)));
   };
@@ -344,13 +344,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     // piece's last key (64-bit path) for a key past the piece end, and for
     // every key of a past-the-end cursor.  The id itself is always read from
     // a valid req_to_token entry.
+    // The table entry is loaded here, one tile ahead; slot_at turns it into
+    // the slot when the tile is loaded, so nothing waits for the entry early.
     auto id_at = [&](const Cursor& cu) -> int {
       const int j = min(cu.j, pt.n - 1);
       const int t_end = pt.t_end(j);
       const int t = (cu.j < pt.n ? cu.t : t_end) + l16;
       const int32_t* row = p.req_to_token + (p.req_to_token_stride > 0 ? (int64_t)(pt.b0 + j) * p.req_to_token_stride
                                                                         : (int64_t)pt.kv[j]);
-      const int id = row[min(t, t_end - 1)];
+      return row[min(t, t_end - 1) >> p.page_shift];
+    };
+    // Slot of this lane's key at cursor cu from its table entry e (page size
+    // 2^page_shift: entry << page_shift plus the position inside the page).
+    auto slot_at = [&](const Cursor& cu, int e) -> int {
+      const int j = min(cu.j, pt.n - 1);
+      const int t_end = pt.t_end(j);
+      const int t = (cu.j < pt.n ? cu.t : t_end) + l16;
+      const int id = (e << p.page_shift) + (min(t, t_end - 1) & ((1 << p.page_shift) - 1));
       if constexpr (OFF32) return t < t_end ? id : -1;
       return id;
     };
@@ -410,11 +420,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     int mA = mask_at(c0);
     int mB = mask_at(c1);
     Tile<D> A, Bt;
-    load_tile<D, OFF32>(A, pv, iA, lane);
+    load_tile<D, OFF32>(A, pv, slot_at(c0, iA), lane);
     if constexpr (MASK) A.vis = __builtin_amdgcn_ballot_w64(mA != 0);
     iA = id_at(c2);
     mA = mask_at(c2);
-    load_tile<D, OFF32>(Bt, pv, iB, lane);
+    load_tile<D, OFF32>(Bt, pv, slot_at(c1, iB), lane);
     if constexpr (MASK) Bt.vis = __builtin_amdgcn_ballot_w64(mB != 0);
     __syncthreads();
 
@@ -481,7 +491,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       compute(X);
       iY = id_at(c3);
       mY = mask_at(c3);
-      load_tile<D, OFF32>(X, pv, iX, lane);
+      load_tile<D, OFF32>(X, pv, slot_at(c2, iX), lane);
       if constexpr (MASK) X.vis = __builtin_amdgcn_ballot_w64(mX != 0);
       c0 = c1;
       c1 = c2;
@@ -706,6 +716,10 @@ hipError_t launch_combine_t(const DecodeLaunch& p, hipStream_t s, const Timing& 
 
 #define ASTR_DECODE_CASES(FN)                       \
   switch (p.head_dim * 100 + p.group) {             \
+    case 3201: return FN<32, 1>(p, s, t);              \
+    case 3202: return FN<32, 2>(p, s, t);              \
+    case 3204: return FN<32, 4>(p, s, t);              \
+    case 3208: return FN<32, 8>(p, s, t);              \
     case 6401: return FN<64, 1>(p, s, t);              \
     case 6402: return FN<64, 2>(p, s, t);              \
     case 6404: return FN<64, 4>(p, s, t);              \
@@ -720,7 +734,7 @@ hipError_t launch_combine_t(const DecodeLaunch& p, hipStream_t s, const Timing& 
 }  // namespace
 
 bool decode_supported(int head_dim, int group) {
-  return (head_dim == 64 || head_dim == 128) && (group == 1 || group == 2 || group == 4 || group == 8);
+  return (head_dim == 32 || head_dim == 64 || head_dim == 128) && (group == 1 || group == 2 || group == 4 || group == 8);
 }
 
 hipError_t launch_decode_split(const DecodeLaunch& p, hipStream_t s, const Timing& t) { ASTR_DECODE_CASES(launch_split_t) }

@@ -39,6 +39,7 @@ struct DecodeLaunch {
   // is hidden when mask[b * mask_stride_req + t] == 0.
   const uint8_t* mask;
   int64_t mask_stride_req;
+  int32_t page_shift;    // log2 page size: slot = (req_to_token[row + t >> s] << s) + (t & (2^s - 1))
 };
 
 // KV append: n_b new tokens per request (1 when qo_indptr is null), written
@@ -56,6 +57,7 @@ struct AppendLaunch {
   int64_t req_to_token_stride;
   const int32_t* kv_indptr;
   const int32_t* qo_indptr;   // null: one new token per request
+  int32_t page_shift;         // log2 page size (see DecodeLaunch)
 };
 
 struct PrefillLaunch {
@@ -80,6 +82,7 @@ struct PrefillLaunch {
   // mask[b * mask_stride_req + i * mask_stride_row + t] == 0 (4-byte aligned).
   const uint8_t* mask;
   int64_t mask_stride_req, mask_stride_row;
+  int32_t page_shift;    // log2 page size (see DecodeLaunch)
   bool off32;            // 32-bit buffer offsets: pool rows of a kv head within pool_range bytes, slot ids < 2^24
   uint32_t pool_range;   // off32: (num_slots - 1) * kv_stride_slot * 2 + head_dim * 2
 };

@@ -132,7 +132,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   constexpr int CPR = D / 8;
   constexpr int RPI = kWave / CPR;
   constexpr int NI = KT / RPI / (kThreads / kWave);
-  auto swz = [](int r) { return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); };
+  // The swizzle stays below the row's chunk count: at D = 32 a row has only
+  // 4 chunks, and an XOR value of 4 or more would address the next row.
+  auto swz = [](int r) { return D == 128 ? 2 * (r & 7) : (D == 64 ? 2 * ((r >> 1) & 3) : (r >> 1) & 3); };
   const int grow0 = RPI * NI * wv + lane / CPR;
   int gchunk[NI];
 #pragma unroll
@@ -143,7 +145,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   if constexpr (OFF32) {
     krs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.k_pool + head_off), (short)0, (int)p.pool_range, 0x00020000);
     vrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.v_pool + head_off), (short)0, (int)p.pool_range, 0x00020000);
-    irs = __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(ids), (short)0, 4 * kv_end, 0x00020000);
+    irs = __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(ids), (short)0,
+                                            4 * (((kv_end - 1) >> p.page_shift) + 1), 0x00020000);
     row_bytes = (uint32_t)(p.kv_stride_slot * 2);
   }
   int id_next[NI];
@@ -151,20 +154,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int t = min(t0 + grow0 + RPI * i, kv_end - 1);
-      if constexpr (OFF32) id_next[i] = __builtin_amdgcn_raw_buffer_load_b32(irs, 4 * t, 0, 0);
-      else id_next[i] = ids[t];
+      // The table entry only; gather adds the page arithmetic where the slot is used.
+      if constexpr (OFF32) id_next[i] = __builtin_amdgcn_raw_buffer_load_b32(irs, 4 * (t >> p.page_shift), 0, 0);
+      else id_next[i] = ids[t >> p.page_shift];
     }
   };
-  auto gather = [&](uint16_t* kdst, uint16_t* vdst) {
+  // Tile starting at key t0: slot of row i's key from its table entry.
+  auto gather = [&](uint16_t* kdst, uint16_t* vdst, int t0) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int row0 = RPI * (NI * wv + i);
+      const int slot = (id_next[i] << p.page_shift) +
+                       (min(t0 + grow0 + RPI * i, kv_end - 1) & ((1 << p.page_shift) - 1));
       if constexpr (OFF32) {
-        const uint32_t voff = __umul24((uint32_t)id_next[i], row_bytes) + 16u * gchunk[i];
+        const uint32_t voff = __umul24((uint32_t)slot, row_bytes) + 16u * gchunk[i];
         __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kdst + row0 * D), 16, voff, 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vdst + row0 * D), 16, voff, 0, 0, 0);
       } else {
-        const int64_t off = (int64_t)id_next[i] * p.kv_stride_slot + head_off + 8 * gchunk[i];
+        const int64_t off = (int64_t)slot * p.kv_stride_slot + head_off + 8 * gchunk[i];
         __builtin_amdgcn_global_load_lds(p.k_pool + off, (lds_void*)(kdst + row0 * D), 16, 0, 0);
         __builtin_amdgcn_global_load_lds(p.v_pool + off, (lds_void*)(vdst + row0 * D), 16, 0, 0);
       }
@@ -179,7 +186,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
   // Tile 0 into stage 0, tile 1's slot ids behind it.
   load_ids(0);
-  gather(sK0, sV0);
+  gather(sK0, sV0, 0);
   load_ids(KT);
 
   // B operand of S^T = K Q^T: lane (r + 16 kb) holds Q[row r][32 ks + 8 kb .. +7] of each row block.
@@ -247,7 +254,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       const int t0 = it * KT;
       const bool more = it + 1 < ntiles;   // uniform
       if (more) {
-        if constexpr (decltype(stage)::value == 0) gather(sK1, sV1); else gather(sK0, sV0);
+        if constexpr (decltype(stage)::value == 0) gather(sK1, sV1, t0 + KT); else gather(sK0, sV0, t0 + KT);
         load_ids(t0 + 2 * KT);
         if constexpr (MASK) load_mask(t0 + KT, mnext);
       }
@@ -442,11 +449,15 @@ hipError_t launch_t(const PrefillLaunch& p, hipStream_t s, const Timing& t) {
 }  // namespace
 
 bool prefill_supported(int head_dim, int group) {
-  return (head_dim == 64 || head_dim == 128) && (group == 1 || group == 2 || group == 4 || group == 8);
+  return (head_dim == 32 || head_dim == 64 || head_dim == 128) && (group == 1 || group == 2 || group == 4 || group == 8);
 }
 
 hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t s, const Timing& t) {
   switch (p.head_dim * 100 + p.group) {
+    case 3201: return launch_t<32, 1>(p, s, t);
+    case 3202: return launch_t<32, 2>(p, s, t);
+    case 3204: return launch_t<32, 4>(p, s, t);
+    case 3208: return launch_t<32, 8>(p, s, t);
     case 6401: return launch_t<64, 1>(p, s, t);
     case 6402: return launch_t<64, 2>(p, s, t);
     case 6404: return launch_t<64, 4>(p, s, t);

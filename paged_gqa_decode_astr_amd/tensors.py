@@ -24,6 +24,7 @@ def to_device(inp: dict, device="cuda") -> dict:
         "req_to_token_stride": int(inp["req_to_token_stride"]),
         "sm_scale": float(inp["sm_scale"]),
         "qo_indptr": None, "qo_indptr_host": None,
+        "page_size": int(inp.get("page_size", 1)),
     }
     if inp.get("k_new") is not None:
         d["k_new"] = bf16_tensor(inp["k_new"], device)
@@ -54,7 +55,8 @@ def run_decode(dev: dict, o=None, lse=None, workspace=None, num_splits=0, stream
     _lib.astr_paged_decode(q, dev["k_pool"], dev["v_pool"], dev["req_to_token"], dev["kv_indptr"],
                            dev["kv_indptr_host"], o, workspace, sm_scale=dev["sm_scale"],
                            req_to_token_stride=dev["req_to_token_stride"], lse=lse, num_splits=num_splits,
-                           stream=stream, timing_events=timing_events, mask=mask)
+                           stream=stream, timing_events=timing_events, mask=mask,
+                           page_size=dev.get("page_size", 1))
     return o
 
 
@@ -63,7 +65,7 @@ def run_append(dev: dict, stream=None, timing_events=None, max_q_len=0):
     _lib.astr_kv_append(dev["k_new"], dev["v_new"], dev["k_pool"], dev["v_pool"], dev["req_to_token"],
                         dev["kv_indptr"], dev["kv_indptr_host"], req_to_token_stride=dev["req_to_token_stride"],
                         qo_indptr=dev["qo_indptr"], qo_indptr_host=dev["qo_indptr_host"], max_q_len=max_q_len,
-                        stream=stream, timing_events=timing_events)
+                        stream=stream, timing_events=timing_events, page_size=dev.get("page_size", 1))
 
 
 def run_decode_append(dev: dict, o=None, lse=None, workspace=None, num_splits=0, stream=None, timing_events=None,
@@ -78,7 +80,8 @@ def run_decode_append(dev: dict, o=None, lse=None, workspace=None, num_splits=0,
     _lib.astr_paged_decode_append(q, dev["k_new"], dev["v_new"], dev["k_pool"], dev["v_pool"], dev["req_to_token"],
                                   dev["kv_indptr"], dev["kv_indptr_host"], o, workspace, sm_scale=dev["sm_scale"],
                                   req_to_token_stride=dev["req_to_token_stride"], lse=lse, num_splits=num_splits,
-                                  stream=stream, timing_events=timing_events, mask=mask)
+                                  stream=stream, timing_events=timing_events, mask=mask,
+                           page_size=dev.get("page_size", 1))
     return o
 
 
@@ -91,7 +94,7 @@ def run_prefill(dev: dict, o=None, lse=None, max_q_len=0, stream=None, timing_ev
                             dev["kv_indptr_host"], dev["qo_indptr"], dev["qo_indptr_host"], o,
                             sm_scale=dev["sm_scale"], req_to_token_stride=dev["req_to_token_stride"], lse=lse,
                             max_q_len=max_q_len, stream=stream, timing_events=timing_events,
-                            non_causal=non_causal, mask=mask)
+                            non_causal=non_causal, mask=mask, page_size=dev.get("page_size", 1))
     return o
 
 

@@ -127,7 +127,7 @@ def _call_prefill(a):
     (lambda a: setattr(a, "sm_scale", float("nan")), 1, "sm_scale"),
     (lambda a: setattr(a, "sm_scale", -0.125), 1, "sm_scale"),
     (lambda a: setattr(a, "sm_scale", 0.0), 1, "sm_scale"),
-    (lambda a: setattr(a, "req_to_token_stride", 3), 1, "exceeds req_to_token_stride"),
+    (lambda a: setattr(a, "req_to_token_stride", 3), 1, "more than req_to_token_stride"),
     (lambda a: setattr(a, "num_slots", 0), 1, "num_slots"),
     (lambda a: setattr(a, "batch", -1), 1, "batch"),
     (lambda a: setattr(a, "qo_indptr", FAKE), 1, "no qo_indptr"),
@@ -215,7 +215,7 @@ def _call_decode_append(a, n, ws=FAKE, nbytes=1 << 30):
     (lambda a, n: setattr(a, "head_dim", 60), "head_dim"),
     (lambda a, n: setattr(a, "kv_stride_slot", 100), "kv strides"),
     (lambda a, n: setattr(a, "num_slots", 0), "num_slots"),
-    (lambda a, n: setattr(a, "req_to_token_stride", 3), "exceeds req_to_token_stride"),
+    (lambda a, n: setattr(a, "req_to_token_stride", 3), "more than req_to_token_stride"),
     (lambda a, n: setattr(a, "qo_indptr", FAKE), "both be set"),
     (lambda a, n: setattr(a, "max_q_len", -1), "max_q_len"),
 ])
@@ -315,3 +315,18 @@ def test_prefill_mask_needs_rows_for_every_query():
     a.mask_stride_req = 4                              # one row, but request 0 has two query rows
     assert _call_prefill(a) == _lib.ASTR_ERR_INVALID_ARG
     assert "query rows" in _lib.astr_last_error()
+
+
+# --------------------------------------------------------------------------- page size validation
+
+@pytest.mark.parametrize("ps,stride,kv,needle", [
+    (3, 8, (0, 3, 7), "page_size"), (-2, 8, (0, 3, 7), "page_size"), (1 << 17, 8, (0, 3, 7), "page_size"),
+    (4, 0, (0, 3, 7), "2-D page table"), (4, 1, (0, 3, 9), "table entries"),
+])
+def test_page_size_validation(ps, stride, kv, needle):
+    """Rejected before any launch (only failing cases: a passing one would launch on placeholder pointers)."""
+    a, keep = _valid_decode_args(kv)    # (0, 3, 9): a seq_len of 6 needs two pages of 4
+    a.page_size = ps
+    a.req_to_token_stride = stride
+    assert _call_decode(a) == _lib.ASTR_ERR_INVALID_ARG
+    assert needle in _lib.astr_last_error()
