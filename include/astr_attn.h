@@ -80,7 +80,7 @@ typedef struct astr_paged_args {
   int32_t batch;          /* B >= 0 requests; B == 0 is a no-op */
   int32_t num_qo_heads;   /* Hq >= 1 */
   int32_t num_kv_heads;   /* Hkv >= 1, Hq % Hkv == 0, Hq / Hkv in {1, 2, 4, 8} */
-  int32_t head_dim;       /* D in {32, 64, 128} */
+  int32_t head_dim;       /* D in {32, 64, 128, 256} */
   float sm_scale;         /* logit scale, finite and > 0, e.g. 1/sqrt(D) */
 
   /* Queries, bf16.  Decode: row b is request b's query.  Prefill: rows in flat

@@ -30,7 +30,8 @@ ceil((x + 1) * W / N) - 1.
 
 Planner (integers only): Wh = forced value if given, else
 min(ceil(WG_PER_CU * num_cus / Hkv), max(1, ceil(N / MIN_TOKENS)), MAX_SPLITS),
-and at least 1.
+and at least 1.  WG_PER_CU is 3, or 1 at head_dim 256 (where the library's
+split kernel fits one work group per CU).
 
 Partial of one piece and query head: m = max of the scaled logits over the
 piece's keys, l = sum exp(s - m), o = sum exp(s - m) v / l (normalised).
@@ -60,9 +61,11 @@ def _ceil_div(a: int, b: int) -> int:
     return -(-a // b)
 
 
-def plan_num_splits(kv_indptr, num_kv_heads, num_cus, forced=0, **consts):
+def plan_num_splits(kv_indptr, num_kv_heads, num_cus, forced=0, head_dim=128, **consts):
     """Work groups per kv head (Wh) for a decode batch."""
     c = dict(DEFAULTS)
+    if head_dim == 256:
+        c["wg_per_cu"] = 1
     c.update(consts)
     if forced and forced > 0:
         return int(forced)

@@ -51,6 +51,8 @@ using astr::ok;
 // a CU at the head_dim-128 kernel's register budget), fewest keys per work
 // group on average (one 16-key tile for each of its wavefronts).
 constexpr int64_t kWgPerCu = 3;
+// At head_dim 256 the split kernel runs one wave per SIMD: one work group per CU.
+int64_t wg_per_cu(int32_t head_dim) { return head_dim == 256 ? 1 : kWgPerCu; }
 constexpr int64_t kMinTokens = 64;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -119,7 +121,7 @@ int validate_common(const astr_paged_args* a, bool prefill, int64_t* total_keys)
   const int group = a->num_qo_heads / a->num_kv_heads;
   const bool supported = prefill ? astr::prefill_supported(a->head_dim, group) : astr::decode_supported(a->head_dim, group);
   if (!supported)
-    return fail(ASTR_ERR_UNSUPPORTED, "no kernel for head_dim=%d and group size %d (head_dim in {32,64,128}, group in {1,2,4,8})",
+    return fail(ASTR_ERR_UNSUPPORTED, "no kernel for head_dim=%d and group size %d (head_dim in {32,64,128,256}, group in {1,2,4,8})",
                 a->head_dim, group);
   if (!(a->sm_scale > 0.f) || a->sm_scale == __builtin_inff())
     return fail(ASTR_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
@@ -246,7 +248,7 @@ int plan_decode_impl(const astr_paged_args* a, int64_t total_keys, int32_t num_c
   } else if (a->num_splits < 0) {
     return fail(ASTR_ERR_INVALID_ARG, "num_splits must be >= 0 (got %d)", a->num_splits);
   } else {
-    const int64_t target = ceil_div(kWgPerCu * (int64_t)num_cus, a->num_kv_heads);
+    const int64_t target = ceil_div(wg_per_cu(a->head_dim) * (int64_t)num_cus, a->num_kv_heads);
     const int64_t by_len = total_keys > 0 ? ceil_div(total_keys, kMinTokens) : 1;
     wh = target < by_len ? target : by_len;
     if (wh > ASTR_DEFAULT_MAX_SPLITS) wh = ASTR_DEFAULT_MAX_SPLITS;

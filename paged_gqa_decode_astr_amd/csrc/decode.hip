@@ -219,8 +219,15 @@ __device__ __forceinline__ void advance(Cursor& c, const PieceTable& pt, int wv)
   settle(c, pt, wv);
 }
 
+// Waves per SIMD the split kernel is built for: three 4-wavefront work groups
+// per CU up to head_dim 128; at head_dim 256 the two K/V tiles, the
+// accumulators and the q operands need the whole register file of one wave
+// (accumulators in AGPRs), so one work group per CU.
+template <int D>
+constexpr int split_waves_per_simd() { return D == 256 ? 1 : 3; }
+
 template <int D, int G, bool OFF32, bool APPEND, bool MASK>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void decode_split_kernel(const DecodeLaunch p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(split_waves_per_simd<D>()))) void decode_split_kernel(const DecodeLaunch p) {
   using S = Shape<D>;
   constexpr int NS = S::kSteps;
   constexpr int NB = S::kDBlocks;
@@ -728,13 +735,18 @@ hipError_t launch_combine_t(const DecodeLaunch& p, hipStream_t s, const Timing& 
     case 12802: return FN<128, 2>(p, s, t);            \
     case 12804: return FN<128, 4>(p, s, t);            \
     case 12808: return FN<128, 8>(p, s, t);            \
+    case 25601: return FN<256, 1>(p, s, t);            \
+    case 25602: return FN<256, 2>(p, s, t);            \
+    case 25604: return FN<256, 4>(p, s, t);            \
+    case 25608: return FN<256, 8>(p, s, t);            \
     default: return hipErrorInvalidValue;           \
   }
 
 }  // namespace
 
 bool decode_supported(int head_dim, int group) {
-  return (head_dim == 32 || head_dim == 64 || head_dim == 128) && (group == 1 || group == 2 || group == 4 || group == 8);
+  return (head_dim == 32 || head_dim == 64 || head_dim == 128 || head_dim == 256) &&
+         (group == 1 || group == 2 || group == 4 || group == 8);
 }
 
 hipError_t launch_decode_split(const DecodeLaunch& p, hipStream_t s, const Timing& t) { ASTR_DECODE_CASES(launch_split_t) }

@@ -70,8 +70,14 @@ struct PShape {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Waves per SIMD: two up to head_dim 128; at 256 the accumulators and
+// operands of a wavefront's 32 rows need the whole register file (one wave,
+// accumulators in AGPRs), and the K/V stages take 128 KB of LDS.
+template <int D>
+constexpr int prefill_waves_per_simd() { return D == 256 ? 1 : 2; }
+
 template <int D, int G, bool OFF32, bool MASK>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(const PrefillLaunch p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefill_waves_per_simd<D>()))) void prefill_kernel(const PrefillLaunch p) {
   using S = PShape<D>;
   constexpr int BQ = kRows / G;   // query positions per work group
   constexpr int NS = S::kSteps;
@@ -134,7 +140,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   constexpr int NI = KT / RPI / (kThreads / kWave);
   // The swizzle stays below the row's chunk count: at D = 32 a row has only
   // 4 chunks, and an XOR value of 4 or more would address the next row.
-  auto swz = [](int r) { return D == 128 ? 2 * (r & 7) : (D == 64 ? 2 * ((r >> 1) & 3) : (r >> 1) & 3); };
+  auto swz = [](int r) { return D >= 128 ? 2 * (r & 7) : (D == 64 ? 2 * ((r >> 1) & 3) : (r >> 1) & 3); };
   const int grow0 = RPI * NI * wv + lane / CPR;
   int gchunk[NI];
 #pragma unroll
@@ -449,7 +455,8 @@ hipError_t launch_t(const PrefillLaunch& p, hipStream_t s, const Timing& t) {
 }  // namespace
 
 bool prefill_supported(int head_dim, int group) {
-  return (head_dim == 32 || head_dim == 64 || head_dim == 128) && (group == 1 || group == 2 || group == 4 || group == 8);
+  return (head_dim == 32 || head_dim == 64 || head_dim == 128 || head_dim == 256) &&
+         (group == 1 || group == 2 || group == 4 || group == 8);
 }
 
 hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t s, const Timing& t) {
@@ -466,6 +473,10 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t s, const Timing& t
     case 12802: return launch_t<128, 2>(p, s, t);
     case 12804: return launch_t<128, 4>(p, s, t);
     case 12808: return launch_t<128, 8>(p, s, t);
+    case 25601: return launch_t<256, 1>(p, s, t);
+    case 25602: return launch_t<256, 2>(p, s, t);
+    case 25604: return launch_t<256, 4>(p, s, t);
+    case 25608: return launch_t<256, 8>(p, s, t);
     default: return hipErrorInvalidValue;
   }
 }

@@ -58,13 +58,14 @@ def test_plan_matches_oracle_random():
         kv = np.concatenate([[0], np.cumsum(L)])
         Hkv = int(rng.choice([1, 2, 4, 8]))
         cus = int(rng.choice([1, 80, 256, 304]))
-        a, keep = _args(kv, Hq=Hkv * 4, Hkv=Hkv)
+        D = int(rng.choice([32, 64, 128, 256]))
+        a, keep = _args(kv, Hq=Hkv * 4, Hkv=Hkv, D=D)
         plan = _lib.astr_plan_decode(a, cus)
-        want = oracle.plan_num_splits(kv, Hkv, cus)
+        want = oracle.plan_num_splits(kv, Hkv, cus, head_dim=D)
         assert plan.num_splits == want
         assert plan.num_partials == want + B - 1
         assert (plan.grid_x, plan.grid_y, plan.grid_z) == (want, Hkv, 1)
-        assert plan.workspace_bytes == _lib.astr_workspace_size(B, Hkv * 4, 128, want)
+        assert plan.workspace_bytes == _lib.astr_workspace_size(B, Hkv * 4, D, want)
 
 
 def test_plan_config_examples():

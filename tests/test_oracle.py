@@ -361,6 +361,8 @@ def test_plan_num_splits_examples():
     assert oracle.plan_num_splits(np.array([0, 1]), 8, 256, forced=9) == 9
     # One kv head on 256 CUs with a long sequence is capped at max_splits.
     assert oracle.plan_num_splits(np.array([0, 1 << 20]), 1, 256) == 256
+    # head_dim 256: one work group per CU -> ceil(256 / 8) = 32 per kv head
+    assert oracle.plan_num_splits(kv, 8, 256, head_dim=256) == 32
 
 
 def test_generator_is_deterministic_and_shaped():

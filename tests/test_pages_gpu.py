@@ -1,4 +1,4 @@
-"""GPU parity of page sizes above one and of head_dim 32.
+"""GPU parity of page sizes above one and of head_dim 32 and 256.
 
 Paged inputs come from the generator's page-by-page layout; expected values
 from the fp64 oracle with the same page size.  The same keys addressed
@@ -153,3 +153,45 @@ def test_head_dim_32_with_pages_and_mask():
                                             mask=mask, page_size=16)
     empty = np.isneginf(ref_lse)
     assert_close(o, np.where(empty[..., None], 0.0, ref_o), "D32 pages mask O")
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 8), (16, 4), (64, 8)])
+def test_head_dim_256_decode_and_prefill(Hq, Hkv):
+    rng = np.random.default_rng(256 + Hq + Hkv)
+    seq = rng.integers(1, 1200, size=10)
+    seq[:4] = [1, 16, 17, 129]
+    inp = build_paged_inputs(seq, Hq, Hkv, 256, 1 << 14, seed=Hq + 256)
+    announce(f"decode head_dim 256 Hq={Hq} Hkv={Hkv}")
+    ref_o, ref_lse = _oracle(inp)
+    for ns in (0, 3):
+        o, lse = _decode(inp, ns)
+        assert_close(o, ref_o, f"D256 decode ns={ns} O")
+        assert_close(lse, ref_lse, f"D256 decode ns={ns} lse", atol=1e-3, rtol=1e-4)
+    q_lens = np.minimum(seq, rng.integers(1, 160, size=10))
+    pin = build_paged_inputs(seq, Hq, Hkv, 256, 1 << 14, seed=Hq + 257, q_lens=q_lens)
+    announce(f"prefill head_dim 256 Hq={Hq} Hkv={Hkv}")
+    pref_o, pref_lse = _oracle(pin)
+    o, lse = _prefill(pin)
+    assert_close(o, pref_o, "D256 prefill O", ulp_check=False)
+    assert_close(lse, pref_lse, "D256 prefill lse", atol=2e-3, rtol=1e-4)
+
+
+def test_head_dim_256_fused_append_pages_and_mask():
+    seq = np.array([300, 1, 77, 640, 33, 1000])
+    inp = build_paged_inputs(seq, 16, 4, 256, 1 << 13, seed=7, page_size=16, new_tokens=1)
+    mask = (np.random.default_rng(8).random((6, 1000)) < 0.8).astype(np.uint8)
+    mt = torch.from_numpy(mask).to(DEV)
+    announce("decode_append head_dim 256, page_size 16, 2-D mask")
+    dev = tensors.to_device(inp, DEV)
+    o = tensors.run_decode_append(dev, workspace=tensors.decode_workspace(6, 16, 256, DEV), mask=mt)
+    dev2 = tensors.to_device(inp, DEV)
+    tensors.run_append(dev2)
+    o2 = tensors.run_decode(dev2, workspace=tensors.decode_workspace(6, 16, 256, DEV), mask=mt)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
+    k2, v2 = oracle.kv_append(inp["k_pool"], inp["v_pool"], inp["k_new"], inp["v_new"], inp["req_to_token"],
+                              inp["req_to_token_stride"], inp["kv_indptr"], page_size=16)
+    ref_o, ref_lse = oracle.paged_attention(inp["q"], k2, v2, inp["req_to_token"], inp["req_to_token_stride"],
+                                            inp["kv_indptr"], inp["sm_scale"], mask=mask, page_size=16)
+    empty = np.isneginf(ref_lse)
+    assert_close(o, np.where(empty[..., None], 0.0, ref_o), "D256 fused append pages mask O")
