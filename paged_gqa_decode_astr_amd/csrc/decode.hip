@@ -16,8 +16,10 @@
 // partial slot w + b.  Ranges are computed on the device from kv_indptr, so a
 // fixed grid stays valid when sequence lengths change.
 //
-// Inside a work group, 4 wavefronts take interleaved 16-key tiles of a piece
-// (a piece of at most 128 keys goes whole to one wavefront).
+// Inside a work group, the tiles of the pieces (16 keys each, in pairs) are
+// laid end to end and cut into 4 contiguous blocks of near-equal length, one
+// per wavefront, so every wavefront loads about the same number of tiles
+// whatever the piece lengths.
 // Per tile and wavefront both products run on the matrix cores:
 //  * S^T = K Q^T with v_mfma_f32_16x16x32_bf16: A is the K tile as loaded
 //    (lane l holds 8 bf16 of key l % 16; four lanes cover 64 contiguous bytes
@@ -39,8 +41,9 @@
 //    than kTau (so weights stay <= 2^kTau); the exact running max is tracked
 //    alongside and the written (m, l) pair uses it.  Keys past the piece end
 //    weigh exactly zero; their loads re-read a valid key of the same request.
-// At the end of a piece the 4 wavefronts merge through LDS and one normalised
-// partial (o, m, l) per query head is written.
+// A piece inside one block is finished by its wavefront, which writes the
+// normalised partial (o, m, l) per query head; a piece crossing block
+// boundaries is merged through LDS once every wavefront is done.
 //
 // Fused KV append (APPEND; [attention_backend.py @47b3ed4], the commit sharing
 // one write-then-gather K/V helper): the new token of request b is its last
@@ -147,77 +150,46 @@ __device__ __forceinline__ void load_tile(Tile<D>& t, const PoolView& pv, int id
 
 // The pieces of a work group (requests its key range touches).  kv_indptr is
 // staged in LDS in windows of kKvStage entries (normally the whole array, in
-// one round trip); pieces are processed in batches that fit the window.
-// Piece j of a batch is request b0 + j; its keys inside the range are
-// positions [t_begin(j), t_end(j)) of that request.
+// one round trip); pieces are processed in windows of at most one q batch
+// (kQBatchRows / G pieces) inside it.  Piece j of a window is request b0 + j;
+// its keys inside the range are positions [t_begin(j), t_end(j)) of that
+// request.
 constexpr int kKvStage = 1024;
 
 struct PieceTable {
   const int32_t* kv;   // LDS copy of kv_indptr[b0 .. b0 + n]
-  int64_t e0, e1;      // the work group's flat key range
+  int e0, e1;          // the work group's flat key range (kv_indptr values are int32)
   int b0, n;
-  __device__ __forceinline__ int t_begin(int j) const { return (int)(max(e0, (int64_t)kv[j]) - kv[j]); }
-  __device__ __forceinline__ int t_end(int j) const { return (int)(min(e1, (int64_t)kv[j + 1]) - kv[j]); }
+  __device__ __forceinline__ int t_begin(int j) const { return max(e0, kv[j]) - kv[j]; }
+  __device__ __forceinline__ int t_end(int j) const { return min(e1, kv[j + 1]) - kv[j]; }
 };
 
-// Pieces of at most kShortKeys keys are processed whole by one wavefront,
-// which writes their partial itself; longer pieces are shared by all
-// wavefronts and merged.  Piece j's owner (short) or first wavefront (long)
-// is (b0 + j) % kWaves, which spreads the extra tiles over the wavefronts.
-constexpr int kShortKeys = 8 * kTile;
-
-__device__ __forceinline__ bool short_piece(const PieceTable& pt, int j) {
-  return pt.t_end(j) - pt.t_begin(j) <= kShortKeys;
-}
-__device__ __forceinline__ int piece_lead(const PieceTable& pt, int j) { return (pt.b0 + j) % kWaves; }
+// Work inside a window of pieces.  Piece j is cut into 32-key pairs of
+// tiles, P_j = ceil(len_j / 32) of them (the last pair may hold masked keys
+// and a fully masked pad tile), and the window's pairs, laid end to end in
+// piece order, are cut into kWaves contiguous blocks of near-equal length:
+// wavefront wv takes pairs [q0, q1) = [Ptot wv / kWaves, Ptot (wv + 1) /
+// kWaves).  Every wavefront therefore loads about the same number of tiles,
+// whatever the piece lengths.  A piece inside one block is finished by its
+// wavefront, which writes the partial; a piece crossing a block boundary is
+// merged through LDS at the end of the window.
+//
+// Per-wavefront piece table in LDS, entry j = {first pair of piece j,
+// t_begin, t_end, kv_indptr[b0 + j]}; entry n holds the pair total.
+struct PieceEntry {
+  int pf, tb, te, kv;
+};
 
 // A wavefront's position in its sequence of tiles: piece j, first key t of
-// the tile.  In a long piece wavefront wv takes tiles t_begin + kTile * (r +
-// kWaves * k) with r = (wv - lead) mod kWaves; in a short piece its owner takes
-// tiles t_begin + kTile * k.  The tile count is rounded up to an even number
-// (the pad tile is fully masked) so that tiles always come in pairs within a
-// piece; `stop` is the padded end, `stride` the step between the wavefront's
-// tiles.  j == n marks the end of the sequence.
+// the tile, end of the wavefront's keys in the piece (stop, a multiple of 32
+// past the segment start), the piece's key end te and the table row of its
+// request.  j == n marks the end of the sequence; te and row then keep the
+// values of a valid piece, so the addresses made from them stay valid.
 struct Cursor {
-  int j, t, stop, stride;
+  int j, t, stop, te;
+  int jr;     // piece whose request addresses the keys (j, or the last one past the end)
+  int ridx;   // its req_to_token row: request index (2-D table) or kv_indptr entry (flat table)
 };
-
-__device__ __forceinline__ void settle(Cursor& c, const PieceTable& pt, int wv) {
-  while (c.j < pt.n) {
-    const int tbeg = pt.t_begin(c.j);
-    const int te = pt.t_end(c.j);
-    const int lead = piece_lead(pt, c.j);
-    if (te - tbeg <= kShortKeys) {
-      if (wv == lead) {
-        int nk = (te - tbeg + kTile - 1) / kTile;
-        nk += nk & 1;
-        c.t = tbeg;
-        c.stride = kTile;
-        c.stop = tbeg + nk * kTile;
-        return;
-      }
-    } else {
-      const int tb = tbeg + kTile * ((wv - lead + kWaves) % kWaves);
-      if (tb < te) {
-        int nk = (te - tb + kWaves * kTile - 1) / (kWaves * kTile);
-        nk += nk & 1;
-        c.t = tb;
-        c.stride = kWaves * kTile;
-        c.stop = tb + nk * kWaves * kTile;
-        return;
-      }
-    }
-    ++c.j;
-  }
-}
-
-__device__ __forceinline__ void advance(Cursor& c, const PieceTable& pt, int wv) {
-  if (c.j >= pt.n) return;
-  c.t += c.stride;
-  if (c.t < c.stop) return;
-  ++c.j;
-  settle(c, pt, wv);
-}
 
 // Waves per SIMD the split kernel is built for: three 4-wavefront work groups
 // per CU up to head_dim 128; at head_dim 256 the two K/V tiles, the
@@ -232,13 +204,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(split_
   constexpr int NS = S::kSteps;
   constexpr int NB = S::kDBlocks;
   constexpr int QSTR = D + 8;   // padded q row (spreads LDS banks)
-  __shared__ float sm_acc[kWaves][G][D];
-  __shared__ float sm_mref[kWaves][G];
-  __shared__ float sm_mx[kWaves][G];
-  __shared__ float sm_l[kWaves][G];
+  __shared__ float sm_acc[kWaves][G][D];         // slot A of each wavefront (shared first piece)
+  __shared__ float4 sm_ml[2][kWaves][G];         // (mref, max, l) of slots A and B
+  __shared__ int4 sm_lead[kWaves];               // merge led by each wavefront: (piece or -1, slot A?, last wavefront)
+  __shared__ PieceEntry sm_tab[kWaves][kQBatchRows + 1];
   constexpr int QB = kQBatchRows / G;   // pieces whose q rows are staged at a time
   __shared__ __align__(16) uint16_t sm_q[QB][G][QSTR];           // q rows of the staged pieces
   __shared__ __align__(16) uint16_t sm_v[kWaves][kTile][S::kVRow];  // per-wavefront V tile
+  static_assert(G * D * sizeof(float) <= sizeof(sm_v[0]), "slot B (G x D floats) must fit a wavefront's V tile area");
   __shared__ int32_t sm_kv[kKvStage];                              // window of kv_indptr starting at kv_base
 
   const int w = blockIdx.x;
@@ -266,13 +239,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(split_
   for (int t = tid; t <= staged; t += kThreads) sm_kv[t] = p.kv_indptr[t];
   const int64_t N_glob = B > staged ? (int64_t)p.kv_indptr[B] : 0;
   __syncthreads();
-  const int64_t N = B > staged ? N_glob : (int64_t)sm_kv[B];
+  // Values read from LDS are the same in every lane; readfirstlane lets the
+  // compiler keep them (and what depends on them) in scalar registers.
+  const int64_t N = B > staged ? N_glob : (int64_t)__builtin_amdgcn_readfirstlane(sm_kv[B]);
   const int64_t W = min((int64_t)p.num_splits, N);
   if (w >= W) return;  // uniform over the work group
 
   PieceTable pt;
-  pt.e0 = ((int64_t)w * N) / W;
-  pt.e1 = ((int64_t)(w + 1) * N) / W;
+  pt.e0 = (int)(((int64_t)w * N) / W);
+  pt.e1 = (int)(((int64_t)(w + 1) * N) / W);
   int bnext;
   if (B <= staged) {
     // Largest b < B with kv_indptr[b] <= e0 (binary search in LDS).
@@ -281,7 +256,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(split_
       const int mid = (lo + hi + 1) >> 1;
       if ((int64_t)sm_kv[mid] <= pt.e0) lo = mid; else hi = mid - 1;
     }
-    bnext = lo;
+    bnext = __builtin_amdgcn_readfirstlane(lo);
   } else {
     bnext = request_of(p.kv_indptr, B, pt.e0);
   }
@@ -289,12 +264,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(split_
   // APPEND: requests bnext .. bnext + n_last - 1 have their last key in this
   // range (those with kv_indptr[b + 1] <= e1; the request holding e0 ends
   // after e0).  Task t copies 16 bytes of the K (wk = 0) or V (wk = 1) row of
-  // kv head g of request bnext + t / (D / 4).  The first kThreads tasks (one
-  // per thread, normally all of them) load now, so their round trip overlaps
-  // the q staging, and store after it; any others are copied right away.
+  // kv head g of request bnext + t / (D / 4).  Every task is copied here,
+  // before the window's set-up (holding the loaded rows across it would
+  // spill them); a barrier before the first tile load orders the stores
+  // before the loads that read them.
   [[maybe_unused]] int n_last = 0;
-  [[maybe_unused]] int32_t a_slot = -1;
-  [[maybe_unused]] uint4 a_val;
   auto kvp = [&](int b) -> int64_t { return b <= staged ? (int64_t)sm_kv[b] : (int64_t)p.kv_indptr[b]; };
   auto append_load = [&](int t, int32_t& slot, uint4& val) {
     const int b = bnext + t / (2 * (D / 8));
@@ -320,8 +294,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(split_
       n_last += __builtin_popcountll(m);
       if (m != ~0ull) break;
     }
-    if (tid < n_last * 2 * (D / 8)) append_load(tid, a_slot, a_val);
-    for (int t = tid + kThreads; t < n_last * 2 * (D / 8); t += kThreads) {
+    for (int t = tid; t < n_last * 2 * (D / 8); t += kThreads) {
       int32_t slot;
       uint4 val;
       append_load(t, slot, val);
@@ -338,14 +311,74 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(split_
       for (int t = tid; t < kKvStage; t += kThreads) sm_kv[t] = p.kv_indptr[min(kv_base + t, B)];
       __syncthreads();
     }
-    if (bnext >= B || (int64_t)sm_kv[bnext - kv_base] >= pt.e1) break;
+    if (bnext >= B || __builtin_amdgcn_readfirstlane(sm_kv[bnext - kv_base]) >= pt.e1) break;
     pt.b0 = bnext;
     pt.kv = sm_kv + (bnext - kv_base);
-    const int room = kKvStage - 1 - (bnext - kv_base);
+    const int room = min(kKvStage - 1 - (bnext - kv_base), QB);
     int n = 0;
-    while (n < room && pt.b0 + n < B && (int64_t)pt.kv[n] < pt.e1) ++n;
+    while (n < room && pt.b0 + n < B && __builtin_amdgcn_readfirstlane(pt.kv[n]) < pt.e1) ++n;
     pt.n = n;
     bnext = pt.b0 + n;
+
+    // Piece table of the window (lane j < n computes entry j; an inclusive
+    // scan over the lanes gives the pair offsets; lane n holds the total).
+    PieceEntry* tab = sm_tab[wv];
+    int incl;
+    {
+      const int jc = min(lane, n - 1);
+      const int tb = pt.t_begin(jc), te = pt.t_end(jc);
+      const int pairs = lane < n ? (te - tb + 2 * kTile - 1) / (2 * kTile) : 0;
+      int x = pairs;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(x, o, kWave);
+        if (lane >= o) x += y;
+      }
+      incl = x;
+      if (lane <= n) tab[lane] = PieceEntry{x - pairs, tb, te, pt.kv[jc]};
+    }
+    const int Ptot = __builtin_amdgcn_readlane(incl, n);
+    const int q0 = Ptot * wv / kWaves;
+    const int q1 = Ptot * (wv + 1) / kWaves;
+    // First piece of the block: the number of pieces that end at or before pair q0.
+    const int jfirst = __builtin_popcountll(__builtin_amdgcn_ballot_w64(lane < n && incl <= q0));
+    auto entry = [&](int j) -> PieceEntry {   // wavefront-uniform read of the table
+      const PieceEntry e = tab[j];
+      return PieceEntry{__builtin_amdgcn_readfirstlane(e.pf), __builtin_amdgcn_readfirstlane(e.tb),
+                        __builtin_amdgcn_readfirstlane(e.te), __builtin_amdgcn_readfirstlane(e.kv)};
+    };
+    auto ridx_of = [&](int j, int kvj) -> int { return p.req_to_token_stride > 0 ? pt.b0 + j : kvj; };
+    auto row_of = [&](const Cursor& cu) -> int64_t {
+      return p.req_to_token_stride > 0 ? (int64_t)cu.ridx * p.req_to_token_stride : (int64_t)cu.ridx;
+    };
+    // The cursor cu entering piece j (at the start of this wavefront's pairs
+    // in it), or ended if the block holds none of it.
+    auto enter = [&](Cursor cu, int j) -> Cursor {
+      Cursor r = cu;
+      r.j = n;
+      r.t = cu.te;
+      if (j < n) {
+        const PieceEntry e = entry(j);
+        const int pf_next = __builtin_amdgcn_readfirstlane(tab[j + 1].pf);
+        const int lo = max(q0, e.pf), hi = min(q1, pf_next);
+        if (lo < hi) {
+          r.j = j;
+          r.jr = j;
+          r.t = e.tb + 2 * kTile * (lo - e.pf);
+          r.stop = e.tb + 2 * kTile * (hi - e.pf);
+          r.te = e.te;
+          r.ridx = ridx_of(j, e.kv);
+        }
+      }
+      return r;
+    };
+    // The next tile of the wavefront's sequence after cu.
+    auto next = [&](Cursor cu) -> Cursor {
+      if (cu.j >= n) return cu;
+      cu.t += kTile;
+      if (cu.t < cu.stop) return cu;
+      return enter(cu, cu.j + 1);
+    };
 
     // Slot id of this lane's key in the tile at cursor cu; -1 (OFF32) or the
     // piece's last key (64-bit path) for a key past the piece end, and for
@@ -354,31 +387,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(split_
     // The table entry is loaded here, one tile ahead; slot_at turns it into
     // the slot when the tile is loaded, so nothing waits for the entry early.
     auto id_at = [&](const Cursor& cu) -> int {
-      const int j = min(cu.j, pt.n - 1);
-      const int t_end = pt.t_end(j);
-      const int t = (cu.j < pt.n ? cu.t : t_end) + l16;
-      const int32_t* row = p.req_to_token + (p.req_to_token_stride > 0 ? (int64_t)(pt.b0 + j) * p.req_to_token_stride
-                                                                        : (int64_t)pt.kv[j]);
-      return row[min(t, t_end - 1) >> p.page_shift];
+      const int t = cu.t + l16;
+      return p.req_to_token[row_of(cu) + (min(t, cu.te - 1) >> p.page_shift)];
     };
     // Slot of this lane's key at cursor cu from its table entry e (page size
     // 2^page_shift: entry << page_shift plus the position inside the page).
     auto slot_at = [&](const Cursor& cu, int e) -> int {
-      const int j = min(cu.j, pt.n - 1);
-      const int t_end = pt.t_end(j);
-      const int t = (cu.j < pt.n ? cu.t : t_end) + l16;
-      const int id = (e << p.page_shift) + (min(t, t_end - 1) & ((1 << p.page_shift) - 1));
-      if constexpr (OFF32) return t < t_end ? id : -1;
+      const int t = cu.t + l16;
+      const int id = (e << p.page_shift) + (min(t, cu.te - 1) & ((1 << p.page_shift) - 1));
+      if constexpr (OFF32) return t < cu.te ? id : -1;
       return id;
     };
     // MASK: the mask byte of this lane's key at cursor cu (read for the
     // clamped key, like the slot id, so it stays inside the request's row).
     auto mask_at = [&](const Cursor& cu) -> int {
       if constexpr (!MASK) return 1;
-      const int j = min(cu.j, pt.n - 1);
-      const int t_end = pt.t_end(j);
-      const int t = min((cu.j < pt.n ? cu.t : t_end) + l16, t_end - 1);
-      return p.mask[(int64_t)(pt.b0 + j) * p.mask_stride_req + t];
+      const int t = min(cu.t + l16, cu.te - 1);
+      return p.mask[(int64_t)(pt.b0 + cu.jr) * p.mask_stride_req + t];
     };
     // q rows of pieces [j0, j0 + nb) -> sm_q[0 .. nb).  The caller brackets
     // this with barriers.
@@ -399,29 +424,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(split_
     // further ahead and are always issued before the data loads that must
     // stay in flight while they are used: vmcnt retires loads in issue order,
     // so an id load issued after a data load could only be waited for
-    // together with it.  Tiles come in pairs within a piece, so buffer A
-    // always holds even tiles and B odd ones and no register copy (which
-    // would wait for its load) is ever needed.
-    // The q rows of the first batch of pieces are staged before any tile
-    // load, so waiting for them waits for nothing else.
-    stage_q(0, min(pt.n, QB));
+    // together with it.  A wavefront's tiles in a piece come in pairs, so
+    // buffer A always holds even tiles and B odd ones and no register copy
+    // (which would wait for its load) is ever needed.
+    // The q rows of the window's pieces are staged before any tile load, so
+    // waiting for them waits for nothing else.
+    stage_q(0, n);
     if constexpr (APPEND) {
       // The new rows are in the pools before any wavefront loads a tile
       // (a work-group barrier orders the stores before the loads).
-      if (first_window && n_last > 0) {   // uniform over the work group
-        if (tid < n_last * 2 * (D / 8)) append_store(tid, a_slot, a_val);
-        __syncthreads();
-      }
+      if (first_window && n_last > 0) __syncthreads();   // uniform over the work group
       first_window = false;
     }
-    Cursor c0{0, 0, 0, 0};
-    settle(c0, pt, wv);
-    Cursor c1 = c0;
-    advance(c1, pt, wv);
-    Cursor c2 = c1;
-    advance(c2, pt, wv);
-    Cursor c3 = c2;
-    advance(c3, pt, wv);
+    Cursor c0;
+    {
+      const PieceEntry e0 = entry(0);
+      c0.jr = 0;
+      c0.te = e0.te;
+      c0.ridx = ridx_of(0, e0.kv);
+      c0.j = n;
+      c0.t = c0.stop = c0.te;
+      if (q0 < q1) c0 = enter(c0, jfirst);
+    }
+    Cursor c1 = next(c0);
+    Cursor c2 = next(c1);
+    Cursor c3 = next(c2);
     int iA = id_at(c0);
     int iB = id_at(c1);
     int mA = mask_at(c0);
@@ -433,12 +460,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(split_
     mA = mask_at(c2);
     load_tile<D, OFF32>(Bt, pv, slot_at(c1, iB), lane);
     if constexpr (MASK) Bt.vis = __builtin_amdgcn_ballot_w64(mB != 0);
+    if (lane == 0) sm_lead[wv] = int4{-1, 0, 0, 0};
     __syncthreads();
 
     float mref = -INFINITY, mx = -INFINITY, lsum = 0.f;
     f32x4 acc[NB];
-    bf16x8 qop[NS];
     int t_end = 0;
+    bf16x8 qop[NS];
     uint16_t* vt = &sm_v[wv][0][0];
 
     // Logits, softmax weights and P.V for the tile in buffer X (cursor c0).
@@ -503,79 +531,116 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(split_
       c0 = c1;
       c1 = c2;
       c2 = c3;
-      advance(c3, pt, wv);
+      c3 = next(c3);
     };
 
-    for (int j = 0; j < pt.n; ++j) {
-      const int jj = j % QB;
-      if (j > 0 && jj == 0) {   // uniform: next batch of q rows
-        __syncthreads();        // every wavefront holds the q rows of its earlier pieces
-        stage_q(j, min(pt.n - j, QB));
-        __syncthreads();
-      }
-      const bool is_short = short_piece(pt, j);   // uniform
-      if (is_short && wv != piece_lead(pt, j)) continue;
+    // The wavefront's pieces, in order.
+    while (c0.j < n) {
+      const int j = c0.j;   // uniform
+      const PieceEntry e = entry(j);
+      const int pf_next = __builtin_amdgcn_readfirstlane(tab[j + 1].pf);
+      const bool owned = e.pf >= q0 && pf_next <= q1;   // the whole piece is in this block
 #pragma unroll
-      for (int s = 0; s < NS; ++s) qop[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&sm_q[jj][hcol][32 * s + 8 * kb]));
+      for (int s = 0; s < NS; ++s) qop[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&sm_q[j][hcol][32 * s + 8 * kb]));
       mref = -INFINITY;
       mx = -INFINITY;
       lsum = 0.f;
 #pragma unroll
       for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-      t_end = pt.t_end(j);
+      t_end = c0.te;
       while (c0.j == j) {
         step(A, iA, iB, mA, mB);
         step(Bt, iB, iA, mB, mA);
       }
-      if (is_short) {
-        // The owner writes the partial: o = acc / l, and (m, l) against the
-        // exact running max.
-        const float l_tot = xor_sum<16, kWave>(lsum);
-        const float mx_tot = xor_max<16, kWave>(mx);
-        if (l16 < G) {
-          const int64_t pidx = (int64_t)(g * G + l16) * p.num_partials + w + pt.b0 + j;
+      // Wavefront totals over the four key groups of each column.
+      const float l_tot = xor_sum<16, kWave>(lsum);
+      const float mx_tot = xor_max<16, kWave>(mx);
+      // The lane's column and key group, opaque to the compiler, so that the
+      // addresses below are formed here instead of being hoisted out of the
+      // tile loop (where they would hold registers the pipeline needs).
+      int col = l16, kg = kb;
+      asm volatile("" : "+v"(col), "+v"(kg));
+      if (owned) {
+        // The wavefront writes the partial: o = acc / l, and (m, l) against
+        // the exact running max.
+        if (col < G) {
+          const int64_t pidx = (int64_t)(g * G + col) * p.num_partials + w + pt.b0 + j;
           const float inv = 1.f / l_tot;
 #pragma unroll
           for (int b = 0; b < NB; ++b)
-            *reinterpret_cast<float4*>(&p.o_part[pidx * D + 16 * b + 4 * kb]) =
+            *reinterpret_cast<float4*>(&p.o_part[pidx * D + 16 * b + 4 * kg]) =
                 make_float4(acc[b][0] * inv, acc[b][1] * inv, acc[b][2] * inv, acc[b][3] * inv);
-          if (kb == 0) {
+          if (kg == 0) {
             p.ml_part[pidx * 2 + 0] = mx_tot * kLn2;
             p.ml_part[pidx * 2 + 1] = l_tot * exp2f(mref - mx_tot);
           }
         }
         continue;
       }
-
-      // Wavefront totals over the four key groups of each column.
-      lsum = xor_sum<16, kWave>(lsum);
-      mx = xor_max<16, kWave>(mx);
-      if (l16 < G) {
+      // A piece shared with other wavefronts: its state goes to slot A (the
+      // block's first piece: sm_acc) or slot B (its last piece, which starts
+      // inside the block: the wavefront's own V tile area, no longer used).
+      const bool slot_a = e.pf <= q0;
+      float* dst = slot_a ? &sm_acc[wv][0][0] : reinterpret_cast<float*>(vt);
+      if (col < G) {
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) sm_acc[wv][l16][16 * b + 4 * kb + r] = acc[b][r];
-        if (kb == 0) {
-          sm_mref[wv][l16] = mref;
-          sm_mx[wv][l16] = mx;
-          sm_l[wv][l16] = lsum;
+          for (int r = 0; r < 4; ++r) dst[col * D + 16 * b + 4 * kg + r] = acc[b][r];
+        if (kg == 0) {
+          sm_ml[slot_a ? 0 : 1][wv][col] = float4{mref, mx_tot, l_tot, 0.f};
         }
       }
-      __syncthreads();
+      if (e.pf >= q0 && lane == 0) {
+        // This wavefront holds the first pairs of the piece: it records the
+        // merge (piece, its slot, the last wavefront holding pairs of it).
+        int wl = kWaves - 1;
+        while (Ptot * wl / kWaves > pf_next - 1) --wl;
+        sm_lead[wv] = int4{j, slot_a ? 1 : 0, wl, 0};
+      }
+    }
+
+    // Merge the pieces that cross block boundaries: piece j led by
+    // wavefront lw is held by wavefronts lw .. wl, in slot A except the
+    // leader's slot B when the piece starts inside its block.
+    __syncthreads();
+    int tid_m = tid;   // opaque copy: the merge's addresses are formed here
+    asm volatile("" : "+v"(tid_m));
+    for (int lw = 0; lw < kWaves - 1; ++lw) {
+      const int4 rec = sm_lead[lw];
+      const int j = __builtin_amdgcn_readfirstlane(rec.x);
+      if (j < 0) continue;
+      const bool lead_a = __builtin_amdgcn_readfirstlane(rec.y) != 0;
+      const int wl = __builtin_amdgcn_readfirstlane(rec.z);
       const int slot = w + pt.b0 + j;
-      for (int idx = tid; idx < G * D; idx += kThreads) {
+      // Wavefronts with an empty block (fewer pairs than wavefronts) hold nothing.
+      bool part[kWaves];
+#pragma unroll
+      for (int k = 0; k < kWaves; ++k) part[k] = k >= lw && k <= wl && Ptot * k / kWaves != Ptot * (k + 1) / kWaves;
+      for (int idx = tid_m; idx < G * D; idx += kThreads) {
         const int hh = idx / D;
         const int d = idx % D;
+        // Every wavefront's state is read at once (one LDS round trip); the
+        // ones not holding the piece are then ignored.
+        float4 ml[kWaves];
+        float a[kWaves];
+#pragma unroll
+        for (int k = 0; k < kWaves; ++k) {
+          const bool in_b = k == lw && !lead_a;
+          ml[k] = sm_ml[in_b ? 1 : 0][k][hh];
+          a[k] = in_b ? reinterpret_cast<const float*>(&sm_v[k][0][0])[hh * D + d] : sm_acc[k][hh][d];
+        }
         float M = -INFINITY;
 #pragma unroll
-        for (int k = 0; k < kWaves; ++k) M = fmaxf(M, sm_mx[k][hh]);
+        for (int k = 0; k < kWaves; ++k)
+          if (part[k]) M = fmaxf(M, ml[k].y);
         float num = 0.f, den = 0.f;
 #pragma unroll
         for (int k = 0; k < kWaves; ++k) {
-          if (sm_mref[k][hh] == -INFINITY) continue;  // wavefront had no key of this piece
-          const float sc = exp2f(sm_mref[k][hh] - M);
-          num = fmaf(sm_acc[k][hh][d], sc, num);
-          den = fmaf(sm_l[k][hh], sc, den);
+          if (!part[k] || ml[k].x == -INFINITY) continue;  // no visible key of this piece in that wavefront
+          const float sc = exp2f(ml[k].x - M);
+          num = fmaf(a[k], sc, num);
+          den = fmaf(ml[k].z, sc, den);
         }
         const int64_t pidx = (int64_t)(g * G + hh) * p.num_partials + slot;
         p.o_part[pidx * D + d] = num / den;
@@ -584,8 +649,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(split_
           p.ml_part[pidx * 2 + 1] = den;
         }
       }
-      __syncthreads();
     }
+    __syncthreads();
   }
 }
 
