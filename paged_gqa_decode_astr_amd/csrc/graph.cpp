@@ -73,20 +73,20 @@ int astr_decode_graph_create(const astr_paged_args* layers, const astr_new_kv* n
   hipGraph_t g = nullptr;
   e = hipStreamEndCapture(s, &g);
   if (st != ASTR_OK) {
-    if (g != nullptr) hipGraphDestroy(g);
+    if (g != nullptr) (void)hipGraphDestroy(g);   // cleanup on the error path; its status is not reported
     return st;
   }
   if (e != hipSuccess) return fail(ASTR_ERR_HIP, "hipStreamEndCapture: %s", hipGetErrorString(e));
   hipGraphExec_t exec = nullptr;
   e = hipGraphInstantiate(&exec, g, nullptr, nullptr, 0);
   if (e != hipSuccess) {
-    hipGraphDestroy(g);
+    (void)hipGraphDestroy(g);
     return fail(ASTR_ERR_HIP, "hipGraphInstantiate: %s", hipGetErrorString(e));
   }
   astr_decode_graph* out = new (std::nothrow) astr_decode_graph;
   if (out == nullptr) {
-    hipGraphExecDestroy(exec);
-    hipGraphDestroy(g);
+    (void)hipGraphExecDestroy(exec);
+    (void)hipGraphDestroy(g);
     return fail(ASTR_ERR_HIP, "out of host memory");
   }
   out->graph = g;

@@ -63,6 +63,23 @@ def test_decode_tile_boundary_lengths():
         assert_close(lse, ref_lse, f"boundaries ns={ns} lse", atol=1e-3, rtol=1e-4)
 
 
+@pytest.mark.parametrize("ns", [1, 2, 4, 9, 23])
+def test_decode_block_split_edges(ns):
+    """Inside a work group the window's 32-key pairs are cut into four
+    contiguous blocks, one per wavefront.  These lengths and split counts give
+    windows with fewer pairs than wavefronts (empty blocks), pieces that start
+    inside a block and cross its end (the leader's second slot), pieces that
+    span three or four blocks, one-key pieces, and windows limited by the q
+    batch (more pieces than one batch holds)."""
+    seq = np.array([1, 33, 64, 65, 2, 31, 32, 97, 1, 1, 1, 200, 5, 129, 3, 1, 1, 40, 96, 1])
+    inp = build_paged_inputs(seq, 16, 4, 128, 4096, seed=77 + ns)
+    announce(f"decode block-split edges num_splits={ns}")
+    o, lse, _, _ = _decode(inp, num_splits=ns)
+    ref_o, ref_lse = oracle_of(inp)
+    assert_close(o, ref_o, f"block split ns={ns} O")
+    assert_close(lse, ref_lse, f"block split ns={ns} lse", atol=1e-3, rtol=1e-4)
+
+
 def test_decode_single_key_returns_v_bits():
     """seq_len 1: the weight is exactly 1, so O must equal the V row bit for bit (right kv head)."""
     inp = build_paged_inputs(np.ones(40, np.int64), 32, 8, 128, 4096, seed=5)
