@@ -223,3 +223,41 @@ def test_head_major_layouts():
         torch.cuda.synchronize()
         r.append(o)
     assert torch.equal(r[0].view(torch.int16), r[1].view(torch.int16))
+
+
+@pytest.mark.parametrize("P,ns", [(1, 0), (1, 5), (16, 0), (64, 3)])
+def test_decode_gather_indices_exact(P, ns):
+    """Gather indices, bit for bit: every V row holds its own slot id
+    (slot = v[0] + 256 * v[1], kv head = v[2]; integers below 256 are exact in
+    bf16), and a mask leaves one key t_b of each request visible, whose
+    weight is then exactly 1.  So each output row is the V row the kernel
+    gathered for position t_b, and it must name the oracle's slot for it
+    (req_to_token lookup, page arithmetic and all)."""
+    rng = np.random.default_rng(700 + P + ns)
+    seq = rng.integers(1, 1500, size=24)
+    seq[:3] = [1, 2, P + 1]
+    inp = build_paged_inputs(seq, 16, 4, 128, 1 << 16, seed=P * 10 + ns, page_size=P)
+    S = inp["v_pool"].shape[0]
+    v = np.zeros((S, 4, 128), np.float32)
+    v[:, :, 0] = np.arange(S)[:, None] % 256
+    v[:, :, 1] = np.arange(S)[:, None] // 256
+    v[:, :, 2] = np.arange(4)[None, :]
+    inp["v_pool"] = (v.view(np.uint32) >> 16).astype(np.uint16)
+    dev = tensors.to_device(inp, DEV)
+    kv = inp["kv_indptr"]
+    ws = tensors.decode_workspace(24, 16, 128, DEV, max_splits=ns)
+    for trial in range(6):
+        t = np.array([rng.integers(0, kv[b + 1] - kv[b]) for b in range(24)])
+        t[0] = 0
+        mask = np.zeros((24, (int(seq.max()) + 3) // 4 * 4), np.uint8)   # row stride: a multiple of 4 bytes
+        mask[np.arange(24), t] = 1
+        announce(f"gather indices page_size={P} num_splits={ns} trial {trial}")
+        o = tensors.run_decode(dev, workspace=ws, num_splits=ns, mask=torch.from_numpy(mask).to(DEV))
+        torch.cuda.synchronize()
+        got = o.float().cpu().numpy()
+        for b in range(24):
+            want = oracle.request_slots(inp["req_to_token"], inp["req_to_token_stride"], kv, b, page_size=P)[t[b]]
+            for h in range(16):
+                row = got[b, h]
+                assert row[0] + 256 * row[1] == want and row[2] == h // 4, (b, h, t[b], row[:3], want)
+                assert np.all(row[3:] == 0)
