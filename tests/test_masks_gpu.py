@@ -261,3 +261,43 @@ def test_decode_gather_indices_exact(P, ns):
                 row = got[b, h]
                 assert row[0] + 256 * row[1] == want and row[2] == h // 4, (b, h, t[b], row[:3], want)
                 assert np.all(row[3:] == 0)
+
+
+@pytest.mark.parametrize("P", [1, 16])
+def test_prefill_gather_indices_exact(P):
+    """The prefill gather (slot ids -> LDS tiles) bit for bit: V rows hold
+    their own slot ids, and a 3-D mask leaves one causally visible key t per
+    query row, whose weight is then exactly 1 (also after rounding to bf16),
+    so each output row names the slot gathered for (b, t)."""
+    rng = np.random.default_rng(900 + P)
+    q_lens = rng.integers(1, 200, size=6)
+    seq = q_lens + rng.integers(0, 700, size=6)
+    inp = build_paged_inputs(seq, 16, 4, 128, 1 << 15, seed=950 + P, q_lens=q_lens, page_size=P)
+    S = inp["v_pool"].shape[0]
+    v = np.zeros((S, 4, 128), np.float32)
+    v[:, :, 0] = np.arange(S)[:, None] % 256
+    v[:, :, 1] = np.arange(S)[:, None] // 256
+    v[:, :, 2] = np.arange(4)[None, :]
+    inp["v_pool"] = (v.view(np.uint32) >> 16).astype(np.uint16)
+    dev = tensors.to_device(inp, DEV)
+    kv, qo = inp["kv_indptr"], inp["qo_indptr"]
+    cols = (int(seq.max()) + 3) // 4 * 4      # row stride: a multiple of 4 bytes
+    mask = np.zeros((6, int(q_lens.max()), cols), np.uint8)
+    pick = {}
+    for b in range(6):
+        L, ql = int(kv[b + 1] - kv[b]), int(q_lens[b])
+        for i in range(ql):
+            t = int(rng.integers(0, L - ql + i + 1))   # within the causal limit of row i
+            mask[b, i, t] = 1
+            pick[(b, i)] = t
+    announce(f"prefill gather indices page_size={P}")
+    o = tensors.run_prefill(dev, mask=torch.from_numpy(mask).to(DEV))
+    torch.cuda.synchronize()
+    got = o.float().cpu().numpy()
+    for b in range(6):
+        slots = oracle.request_slots(inp["req_to_token"], inp["req_to_token_stride"], kv, b, page_size=P)
+        for i in range(int(q_lens[b])):
+            want = slots[pick[(b, i)]]
+            rows = got[int(qo[b]) + i]
+            assert np.all(rows[:, 0] + 256 * rows[:, 1] == want), (b, i, rows[:, :2], want)
+            assert np.all(rows[:, 2] == np.arange(16) // 4) and np.all(rows[:, 3:] == 0)
