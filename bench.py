@@ -153,6 +153,7 @@ def main(argv=None):
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-append", action="store_true", help="skip the KV append + decode leg")
     ap.add_argument("--no-graph", action="store_true", help="skip the whole-step graph leg")
+    ap.add_argument("--no-warm", action="store_true", help="skip the warm-cache reference leg")
     ap.add_argument("--probe", action="store_true", help="also measure torch copy / row-gather bandwidth ceilings")
     ap.add_argument("--num-splits", type=int, default=0, help="decode work groups per kv head (0 = library plan)")
     args = ap.parse_args(argv)
@@ -234,19 +235,20 @@ def main(argv=None):
 
     # Warm: the same input set every call, so K/V can stay in the 256 MB
     # Infinity Cache and the L2s (a reference point; the value above is cold).
-    log("[bench] warm leg (one input set)")
-    for _ in range(args.warmup):
-        step(0)
-    torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
-        step(0)
-    stop.record()
-    torch.cuda.synchronize()
-    warm_ms = start.elapsed_time(stop) / args.steps
-    out["warm"] = {"us_per_call": round(warm_ms * 1e3, 2),
-                   "GBs": round(profiling.decode_bytes(sets[0][0]) / (warm_ms * 1e-3) / 1e9, 1),
-                   "note": "set 0 every call (caches warm); not the headline value"}
+    if not args.no_warm:
+        log("[bench] warm leg (one input set)")
+        for _ in range(args.warmup):
+            step(0)
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(args.steps):
+            step(0)
+        stop.record()
+        torch.cuda.synchronize()
+        warm_ms = start.elapsed_time(stop) / args.steps
+        out["warm"] = {"us_per_call": round(warm_ms * 1e3, 2),
+                       "GBs": round(profiling.decode_bytes(sets[0][0]) / (warm_ms * 1e-3) / 1e9, 1),
+                       "note": "set 0 every call (caches warm); not the headline value"}
 
     if not args.no_append:
         log("[bench] append leg: KV append + decode, separate vs fused")

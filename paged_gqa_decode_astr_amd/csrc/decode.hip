@@ -204,7 +204,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(split_
   constexpr int NS = S::kSteps;
   constexpr int NB = S::kDBlocks;
   constexpr int QSTR = D + 8;   // padded q row (spreads LDS banks)
-  __shared__ float sm_acc[kWaves][G][D];         // slot A of each wavefront (shared first piece)
+  __shared__ __align__(16) float sm_acc[kWaves][G][D];   // slot A of each wavefront (shared first piece)
   __shared__ float4 sm_ml[2][kWaves][G];         // (mref, max, l) of slots A and B
   __shared__ int4 sm_lead[kWaves];               // merge led by each wavefront: (piece or -1, slot A?, last wavefront)
   __shared__ PieceEntry sm_tab[kWaves][kQBatchRows + 1];
@@ -617,37 +617,37 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(split_
       bool part[kWaves];
 #pragma unroll
       for (int k = 0; k < kWaves; ++k) part[k] = k >= lw && k <= wl && Ptot * k / kWaves != Ptot * (k + 1) / kWaves;
-      for (int idx = tid_m; idx < G * D; idx += kThreads) {
-        const int hh = idx / D;
-        const int d = idx % D;
+      // Thread task: two consecutive d of one head (G * D / 2 tasks).
+      for (int task = tid_m; task < G * D / 2; task += kThreads) {
+        const int hh = task / (D / 2);
+        const int d = 2 * (task % (D / 2));
         // Every wavefront's state is read at once (one LDS round trip); the
         // ones not holding the piece are then ignored.
         float4 ml[kWaves];
-        float a[kWaves];
+        float2 a[kWaves];
 #pragma unroll
         for (int k = 0; k < kWaves; ++k) {
           const bool in_b = k == lw && !lead_a;
           ml[k] = sm_ml[in_b ? 1 : 0][k][hh];
-          a[k] = in_b ? reinterpret_cast<const float*>(&sm_v[k][0][0])[hh * D + d] : sm_acc[k][hh][d];
+          const float* src = in_b ? reinterpret_cast<const float*>(&sm_v[k][0][0]) : &sm_acc[k][0][0];
+          a[k] = *reinterpret_cast<const float2*>(&src[hh * D + d]);
         }
         float M = -INFINITY;
 #pragma unroll
         for (int k = 0; k < kWaves; ++k)
           if (part[k]) M = fmaxf(M, ml[k].y);
-        float num = 0.f, den = 0.f;
+        float num0 = 0.f, num1 = 0.f, den = 0.f;
 #pragma unroll
         for (int k = 0; k < kWaves; ++k) {
           if (!part[k] || ml[k].x == -INFINITY) continue;  // no visible key of this piece in that wavefront
           const float sc = exp2f(ml[k].x - M);
-          num = fmaf(a[k], sc, num);
+          num0 = fmaf(a[k].x, sc, num0);
+          num1 = fmaf(a[k].y, sc, num1);
           den = fmaf(ml[k].z, sc, den);
         }
         const int64_t pidx = (int64_t)(g * G + hh) * p.num_partials + slot;
-        p.o_part[pidx * D + d] = num / den;
-        if (d == 0) {
-          p.ml_part[pidx * 2 + 0] = M * kLn2;
-          p.ml_part[pidx * 2 + 1] = den;
-        }
+        *reinterpret_cast<float2*>(&p.o_part[pidx * D + d]) = make_float2(num0 / den, num1 / den);
+        if (d == 0) *reinterpret_cast<float2*>(&p.ml_part[pidx * 2]) = make_float2(M * kLn2, den);
       }
     }
     __syncthreads();

@@ -279,7 +279,7 @@ def main(argv=None):
         return _pmc(args)
     # Default: the decode timing legs of bench.py only (its graph and append legs launch the same
     # kernel at other shapes, which would enter the kernel's average).
-    return _trace(args, bench_args or ["--cpu-seconds", "0", "--no-graph", "--no-append"])
+    return _trace(args, bench_args or ["--cpu-seconds", "0", "--no-graph", "--no-append", "--no-warm"])
 
 
 if __name__ == "__main__":
