@@ -350,9 +350,10 @@ class DecodeGraph:
     """A captured multi-layer decode step (astr_decode_graph_*): warm-up, capture, replay.
 
     layers: one dict per layer with the astr_paged_decode tensors (q, k_pool, v_pool, req_to_token,
-    kv_indptr, kv_indptr_host, o, and optionally lse, k_new / v_new for the fused append) plus
-    sm_scale and req_to_token_stride.  Every tensor must stay allocated while the graph is used;
-    a launch reads their current contents.  num_splits fixes the plan (required for capture)."""
+    kv_indptr, kv_indptr_host, o, and optionally lse, mask, k_new / v_new for the fused append) plus
+    sm_scale, req_to_token_stride and optionally page_size.  The graph holds the device addresses it
+    was captured with, so this object keeps a reference to every layer tensor and the workspace until
+    close(); a launch reads their current contents.  num_splits fixes the plan (required for capture)."""
 
     def __init__(self, layers, workspace, *, num_splits, stream):
         lib = load_library()
@@ -366,18 +367,23 @@ class DecodeGraph:
         for i, L in enumerate(layers):
             a, k = make_args(L["q"], L["k_pool"], L["v_pool"], L["req_to_token"], L["kv_indptr"],
                              L["kv_indptr_host"], L["o"], sm_scale=L["sm_scale"],
-                             req_to_token_stride=L["req_to_token_stride"], lse=L.get("lse"), num_splits=num_splits)
+                             req_to_token_stride=L["req_to_token_stride"], lse=L.get("lse"), num_splits=num_splits,
+                             mask=L.get("mask"), page_size=L.get("page_size", 1))
             arr[i] = a
             keep.append(k)
             if nkv is not None:
                 nkv[i] = make_new_kv(L["k_new"], L["v_new"])
         self._stream = stream
+        self._handle = None
+        self._keep = None
         handle = ctypes.c_void_p()
         ws_bytes = workspace.numel() * workspace.element_size()
         _check(lib.astr_decode_graph_create(arr, nkv, n, _ptr(workspace), ws_bytes, ctypes.c_void_p(stream.cuda_stream),
                                             ctypes.byref(handle)))
         self._handle = handle
         self.num_layers = n
+        # The captured kernels read and write these tensors by address: keep them alive with the graph.
+        self._keep = (list(layers), workspace, keep, arr, nkv)
 
     def launch(self, stream=None):
         s = self._stream if stream is None else stream
@@ -387,6 +393,7 @@ class DecodeGraph:
         if self._handle is not None and self._handle.value:
             _check(load_library().astr_decode_graph_destroy(self._handle))
         self._handle = None
+        self._keep = None
 
     def __del__(self):
         try:

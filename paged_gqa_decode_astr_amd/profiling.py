@@ -1,6 +1,6 @@
 """rocprofv3 measurements of the decode kernels.
 
-Three subcommands:
+Subcommands:
 
   workload  the program that is profiled: warm-up and timed decode calls over
             rotating seeded input sets, then a plain copy kernel of known size
@@ -9,6 +9,14 @@ Three subcommands:
             WRITE_SIZE), scales the split kernel's per-dispatch counts by what
             the same counters read for the copy kernel, and writes
             profiles/decode_split_<config>_pmc.{json,md}.
+  prefill-workload
+            the profiled prefill program: warm-up and timed prefill calls on
+            one seeded prefill_b8 input set.
+  prefill-pmc
+            runs `prefill-workload` under rocprofv3 --pmc passes of shader
+            counters (matrix-core busy cycles and bf16 MFMA operations, VALU and
+            LDS activity, wave occupancy) and writes
+            profiles/prefill_kernel_<config>_pmc.{json,md}.
   trace     runs bench.py under rocprofv3 --kernel-trace --stats and writes
             profiles/decode_<config>_kernel_trace.md.
 
@@ -69,8 +77,15 @@ def append_bytes(inp):
     return B * Hkv * D * 2 * 2 * 2 + B * 4
 
 
+PREFILL_SOURCES = ("paged_gqa_decode_astr_amd/csrc/prefill.hip", "paged_gqa_decode_astr_amd/csrc/api.cpp")
+
+
+def sources_digest_of(path):
+    return hashlib.sha256(open(os.path.join(ROOT, path), "rb").read()).hexdigest()
+
+
 def sources_digest():
-    return {p: hashlib.sha256(open(os.path.join(ROOT, p), "rb").read()).hexdigest() for p in TRAFFIC_SOURCES}
+    return {p: sources_digest_of(p) for p in TRAFFIC_SOURCES}
 
 
 def read_traffic(config):
@@ -222,6 +237,121 @@ def _pmc(args):
     return 0
 
 
+# Shader-counter passes for the prefill kernel.  One rocprofv3 run per pass: a
+# run holds at most 8 SQ counters and 2 GRBM counters.
+PREFILL_PASSES = (
+    ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_MFMA", "SQ_BUSY_CU_CYCLES",
+     "SQ_WAVE_CYCLES", "SQ_WAVES", "SQ_ACTIVE_INST_VALU", "SQ_VALU_MFMA_COEXEC_CYCLES", "GRBM_GUI_ACTIVE"),
+    ("SQ_ACTIVE_INST_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_WAIT_INST_LDS", "SQ_INSTS_LDS",
+     "SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32", "SQ_CYCLES", "GRBM_GUI_ACTIVE"),
+)
+MI355X_SIMDS = 256 * 4
+MI355X_XCDS = 8
+MI355X_CLOCK_GHZ = 2.4
+
+
+def _prefill_workload(args):
+    import torch
+
+    from . import _lib, tensors
+    from .workloads import make_inputs
+    _lib.load_library()
+    inp = make_inputs(args.config, 0)
+    d = tensors.to_device(inp, "cuda")
+    o = torch.empty_like(d["q"])
+    lse = torch.empty(d["q"].shape[0], d["q"].shape[1], dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(args.warmup + args.calls):
+        tensors.run_prefill(d, o=o, lse=lse)
+    torch.cuda.synchronize()
+    print(f"[prefill-workload] {args.config}: {args.warmup}+{args.calls} prefill calls", flush=True)
+    return 0
+
+
+def prefill_flops(inp):
+    """Algorithmic FLOPs of one prefill call: 4 * D * Hq per causally visible (query row, key) pair."""
+    _, Hq, D = inp["q"].shape
+    kv, qo = inp["kv_indptr"], inp["qo_indptr"]
+    pairs = 0
+    for b in range(len(kv) - 1):
+        L = int(kv[b + 1] - kv[b])
+        qb = int(qo[b + 1] - qo[b])
+        pairs += qb * (L - qb) + qb * (qb + 1) // 2
+    return 4 * D * Hq * pairs
+
+
+def _prefill_pmc(args):
+    from .workloads import make_inputs
+    raw = os.path.abspath(args.raw)
+    os.makedirs(raw, exist_ok=True)
+    wl = [sys.executable, "-m", "paged_gqa_decode_astr_amd.profiling", "prefill-workload", "--config", args.config,
+          "--warmup", str(args.warmup), "--calls", str(args.calls)]
+    vals = {}
+    passes = []
+    for i, counters in enumerate(PREFILL_PASSES):
+        out = os.path.join(raw, f"prefill_pass{i}")
+        cmd = ["rocprofv3", "--pmc", *counters, "--output-format", "csv", "-d", out, "-o", "run", "--"] + wl
+        passes.append("cd /tmp && TMPDIR=/tmp timeout -s KILL {t} ".format(t=args.timeout) +
+                      " ".join(shlex.quote(c) for c in cmd).replace(out, f"<raw>/prefill_pass{i}"))
+        if not args.summarize_only:
+            _run_profiler(cmd, os.path.join(raw, f"prefill_pass{i}.log"), args.timeout)
+        rows = _counter_rows(out)
+        for c in counters:
+            key = c if c != "GRBM_GUI_ACTIVE" else f"GRBM_GUI_ACTIVE_pass{i}"
+            vals[key] = statistics.mean(_per_dispatch(rows, c, "prefill_kernel", last=args.calls))
+    inp = make_inputs(args.config, 0)
+    algo = prefill_flops(inp)
+    # GRBM_GUI_ACTIVE comes summed over the 8 XCDs (one GRBM each): per-XCD cycles of the dispatch.
+    gui = vals["GRBM_GUI_ACTIVE_pass0"] / MI355X_XCDS
+    gui1 = vals["GRBM_GUI_ACTIVE_pass1"] / MI355X_XCDS
+    mfma_flops = vals["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+    derived = {
+        "dispatch_us (GUI active cycles per XCD / 2.4 GHz)": gui / (MI355X_CLOCK_GHZ * 1e3),
+        "mfma_util_pct (MFMA busy cycles / (GUI active cycles x 1024 SIMDs))":
+            100 * vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * MI355X_SIMDS),
+        "mfma_bf16_flops_per_dispatch": mfma_flops,
+        "mfma_busy_cycles_per_mfma": vals["SQ_VALU_MFMA_BUSY_CYCLES"] / max(1.0, vals["SQ_INSTS_MFMA"]),
+        "algorithmic_flops_per_dispatch (causally visible pairs)": algo,
+        "mfma_flops_over_algorithmic": mfma_flops / algo,
+        "valu_busy_pct (VALU active quad-cycles x 4 / (GUI cycles x 1024 SIMDs))":
+            100 * vals["SQ_ACTIVE_INST_VALU"] * 4 / (gui * MI355X_SIMDS),
+        "lds_active_pct (LDS active quad-cycles x 4 / (GUI cycles x 256 CUs))":
+            100 * vals["SQ_ACTIVE_INST_LDS"] * 4 / (gui1 * 256),
+        "lds_bank_conflict_cycles_over_lds_active": vals["SQ_LDS_BANK_CONFLICT"] / max(1.0, vals["SQ_LDS_IDX_ACTIVE"]),
+        "mean_resident_waves_per_cu (wave quad-cycles x 4 / (GUI cycles x 256))":
+            vals["SQ_WAVE_CYCLES"] * 4 / (gui * 256),
+        "mfma_valu_coexec_over_mfma_busy": vals["SQ_VALU_MFMA_COEXEC_CYCLES"] / max(1.0, vals["SQ_VALU_MFMA_BUSY_CYCLES"]),
+    }
+    rec = {
+        "kernel": "prefill_kernel", "workload": args.config,
+        "command": f"python3 -m paged_gqa_decode_astr_amd.profiling prefill-pmc --config {args.config} "
+                   f"--warmup {args.warmup} --calls {args.calls}",
+        "passes": passes, "sources": {p: sources_digest_of(p) for p in PREFILL_SOURCES},
+        "dispatches": args.calls, "counters_mean_per_dispatch": vals, "derived": derived,
+    }
+    os.makedirs(PROFILES, exist_ok=True)
+    base = args.out or os.path.join(PROFILES, f"prefill_kernel_{args.config}_pmc")
+    with open(base + ".json", "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    with open(base + ".md", "w") as fh:
+        fh.write(f"# prefill_kernel shader counters, workload {args.config}\n\n")
+        fh.write(f"Command: `{rec['command']}`\n\nPasses (each its own rocprofv3 run):\n\n")
+        for c in passes:
+            fh.write(f"- `{c}`\n")
+        fh.write("\n| counter (mean per dispatch, summed over instances) | value |\n|---|---|\n")
+        for k, v in vals.items():
+            fh.write(f"| {k} | {v:.6g} |\n")
+        fh.write("\n| derived | value |\n|---|---|\n")
+        for k, v in derived.items():
+            fh.write(f"| {k} | {v:.4g} |\n")
+        fh.write("\nGRBM_GUI_ACTIVE counts GPU-active cycles of a dispatch, summed over the 8 XCDs; MI355X has 256 CUs "
+                 "of 4 SIMDs (SIMD-cycle figures divide by 1024 SIMDs, CU figures by 256 CUs). "
+                 "SQ_INSTS_VALU_MFMA_MOPS_BF16 counts bf16 MFMA math operations / 512.\n")
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def _trace(args, bench_args):
     raw = os.path.abspath(args.raw)
     os.makedirs(raw, exist_ok=True)
@@ -263,7 +393,7 @@ def main(argv=None):
         i = argv.index("--")
         argv, bench_args = argv[:i], argv[i + 1:]
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("mode", choices=["workload", "pmc", "trace"])
+    ap.add_argument("mode", choices=["workload", "pmc", "prefill-workload", "prefill-pmc", "trace"])
     ap.add_argument("--config", default="decode_b32")
     ap.add_argument("--sets", type=int, default=4)
     ap.add_argument("--warmup", type=int, default=8)
@@ -272,11 +402,20 @@ def main(argv=None):
     ap.add_argument("--raw", default="gpurun_out/prof", help="directory for rocprofv3's raw output")
     ap.add_argument("--timeout", type=int, default=240, help="seconds before a profiler run is killed")
     ap.add_argument("--top", type=int, default=8, help="kernels listed in the trace summary")
+    ap.add_argument("--summarize-only", action="store_true",
+                    help="prefill-pmc: write the summary from the raw output already under --raw (no profiler run)")
+    ap.add_argument("--out", default=None, help="prefill-pmc: summary file stem (default profiles/prefill_kernel_<config>_pmc)")
     args = ap.parse_args(argv)
     if args.mode == "workload":
         return _workload(args)
     if args.mode == "pmc":
         return _pmc(args)
+    if args.mode == "prefill-workload":
+        return _prefill_workload(args)
+    if args.mode == "prefill-pmc":
+        if args.config == "decode_b32":
+            args.config = "prefill_b8"
+        return _prefill_pmc(args)
     # Default: the decode timing legs of bench.py only (its graph and append legs launch the same
     # kernel at other shapes, which would enter the kernel's average).
     return _trace(args, bench_args or ["--cpu-seconds", "0", "--no-graph", "--no-append", "--no-warm"])

@@ -41,17 +41,17 @@ def _device_layers(inps):
     return layers
 
 
-def _eager(inps, fused):
+def _eager(inps, fused, masks=None):
     """Outputs of the same per-layer calls made eagerly (fresh device copies)."""
     res = []
-    for inp in inps:
+    for l, inp in enumerate(inps):
         d = tensors.to_device(inp, DEV)
         B, Hq, D = inp["q"].shape
         o = torch.empty(B, Hq, D, dtype=torch.bfloat16, device=DEV)
         lse = torch.empty(B, Hq, dtype=torch.float32, device=DEV)
         ws = tensors.decode_workspace(B, Hq, D, DEV, max_splits=NS)
         run = tensors.run_decode_append if fused else tensors.run_decode
-        run(d, o=o, lse=lse, workspace=ws, num_splits=NS)
+        run(d, o=o, lse=lse, workspace=ws, num_splits=NS, mask=None if masks is None else masks[l])
         res.append((o, lse, d))
     torch.cuda.synchronize()
     return res
@@ -102,6 +102,78 @@ def test_graph_replays_match_eager(fused):
         s.synchronize()
         _check_against(layers, ref, f"replay {rep}")
         del junk
+    g.close()
+
+
+@pytest.mark.parametrize("masked", [False, True])
+@pytest.mark.parametrize("fused", [False, True])
+def test_graph_with_pages_and_mask(fused, masked):
+    """Layers with a page size of 16 (a 2-D table of page ids) and, optionally, a 2-D mask: the
+    captured step carries each layer's page size and mask, bit for bit like the eager calls."""
+    B, L, P, stride_keys = 5, 2, 16, 1600
+    rng = np.random.default_rng(61 + 2 * fused + masked)
+    inps = []
+    for l in range(L):
+        seq = rng.integers(1, stride_keys, size=B)
+        inps.append(build_paged_inputs(seq, 32, 8, 128, 1 << 15, seed=6100 + 10 * l + fused, page_size=P,
+                                       new_tokens=1 if fused else None))
+    masks = None
+    if masked:
+        masks = []
+        for inp in inps:
+            m = (rng.random((B, stride_keys)) < 0.6).astype(np.uint8)
+            m[:, 0] = 1
+            masks.append(torch.from_numpy(m).to(DEV))
+    layers = _device_layers(inps)
+    for l, d in enumerate(layers):
+        assert d["page_size"] == P
+        if masked:
+            d["mask"] = masks[l]
+    ws = tensors.decode_workspace(B, 32, 128, DEV, max_splits=NS)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    announce(f"graph capture page_size={P} masked={masked} fused={fused}")
+    g = _lib.DecodeGraph(layers, ws, num_splits=NS, stream=s)
+    s.synchronize()
+    ref = _eager(inps, fused, masks)
+    _check_against(layers, ref, "live run")
+    for rep in range(2):
+        for d in layers:
+            d["o"].fill_(float("nan"))
+            d["lse"].fill_(float("nan"))
+        torch.cuda.synchronize()
+        announce(f"graph replay {rep} page_size={P} masked={masked} fused={fused}")
+        with torch.cuda.stream(s):
+            g.launch()
+        s.synchronize()
+        _check_against(layers, ref, f"replay {rep}")
+    g.close()
+
+
+def test_graph_keeps_its_tensors_alive():
+    """The graph object holds the captured tensors: dropping the caller's references and allocating
+    new memory does not disturb a replay."""
+    B, L = 4, 2
+    inps = _layer_inputs(B, L, seed=71)
+    layers = _device_layers(inps)
+    ws = tensors.decode_workspace(B, 32, 128, DEV, max_splits=NS)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    announce("graph keeps its tensors alive")
+    g = _lib.DecodeGraph(layers, ws, num_splits=NS, stream=s)
+    s.synchronize()
+    o_ptrs = [d["o"].data_ptr() for d in layers]
+    del layers, ws
+    filler = [torch.full((1 << 20,), 3.0, device=DEV) for _ in range(8)]   # would reuse freed blocks
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        g.launch()
+    s.synchronize()
+    kept = g._keep[0]
+    assert [d["o"].data_ptr() for d in kept] == o_ptrs
+    ref = _eager(inps, False)
+    _check_against(kept, ref, "replay after the caller dropped its references")
+    assert all(bool((f == 3.0).all()) for f in filler)
     g.close()
 
 
