@@ -37,7 +37,9 @@
  *  - Ownership: the caller owns every buffer (q, o, lse, pools, index arrays,
  *    workspace).  The library never allocates or frees device memory, never
  *    synchronises the device, never copies host->device and keeps no pointer
- *    after a call returns.  *_host arrays are read only during the call.
+ *    after a call returns.  *_host arrays are read only during the call.  The
+ *    one library-owned buffer is the fixed device scratch array of the
+ *    allocation-free entry point (astr_paged_decode_noalloc).
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
  *    null stream).  With a fixed plan (num_splits / max_q_len set) the enqueued
  *    work reads lengths only from device memory, so a call can be captured into
@@ -63,7 +65,7 @@
 extern "C" {
 #endif
 
-#define ASTR_ABI_VERSION 4
+#define ASTR_ABI_VERSION 5
 
 /* Default cap on work groups per kv head in an automatic decode plan. */
 #define ASTR_DEFAULT_MAX_SPLITS 256
@@ -190,6 +192,26 @@ int astr_plan_decode(const astr_paged_args* a, int32_t num_cus, astr_decode_plan
  * writes o (and lse).  workspace_bytes must be >= the plan's workspace_bytes.
  * Returns astr_status. */
 int astr_paged_decode(const astr_paged_args* a, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of the library's own device scratch array used by
+ * astr_paged_decode_noalloc (one copy per GPU, held until the process ends). */
+#define ASTR_NOALLOC_SCRATCH_BYTES (32ull << 20)
+
+/* Allocation-free paged GQA decode, for callers that cannot allocate device
+ * memory or hand over a workspace at call time (code under stream capture,
+ * tight serving loops, harnesses that forbid allocation).  Same arguments,
+ * kernels and result bits as astr_paged_decode with the same plan, but the
+ * split partials go to a file-scope device array of
+ * ASTR_NOALLOC_SCRATCH_BYTES bytes owned by the library (each GPU holds its
+ * own copy from its first call until the process ends; its address is looked
+ * up once per device).  The call allocates and frees nothing.
+ * Limits and sharing: a plan whose partials need more than
+ * ASTR_NOALLOC_SCRATCH_BYTES (astr_plan_decode's workspace_bytes) is rejected
+ * with ASTR_ERR_WORKSPACE before anything is enqueued.  Every call on one GPU
+ * uses the same array, which keeps the last call's contents (nothing in it
+ * needs clearing): calls that overlap on one GPU, e.g. on two streams, race
+ * and give undefined results; serialise them.  Returns astr_status. */
+int astr_paged_decode_noalloc(const astr_paged_args* a, void* stream);
 
 /* Ragged paged prefill with causal offset seq_len - q_len per request.
  * Needs no workspace (NULL / 0 allowed).  Returns astr_status. */

@@ -23,8 +23,10 @@ ASTR_ERR_UNSUPPORTED = 2
 ASTR_ERR_WORKSPACE = 3
 ASTR_ERR_HIP = 4
 DEFAULT_MAX_SPLITS = 256
+NOALLOC_SCRATCH_BYTES = 32 << 20   # ASTR_NOALLOC_SCRATCH_BYTES
 
-EXPORTED = ("astr_workspace_size", "astr_plan_decode", "astr_paged_decode", "astr_paged_prefill",
+EXPORTED = ("astr_workspace_size", "astr_plan_decode", "astr_paged_decode", "astr_paged_decode_noalloc",
+            "astr_paged_prefill",
             "astr_kv_append", "astr_paged_decode_append", "astr_decode_graph_create", "astr_decode_graph_launch",
             "astr_decode_graph_destroy", "astr_last_error", "astr_abi_version")
 
@@ -89,6 +91,8 @@ def load_library(path: str = LIB_PATH):
         f = getattr(lib, fn)
         f.restype = ctypes.c_int
         f.argtypes = [ctypes.POINTER(PagedArgs), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.astr_paged_decode_noalloc.restype = ctypes.c_int
+    lib.astr_paged_decode_noalloc.argtypes = [ctypes.POINTER(PagedArgs), ctypes.c_void_p]
     lib.astr_kv_append.restype = ctypes.c_int
     lib.astr_kv_append.argtypes = [ctypes.POINTER(PagedArgs), ctypes.POINTER(NewKV), ctypes.c_void_p]
     lib.astr_paged_decode_append.restype = ctypes.c_int
@@ -231,6 +235,18 @@ def astr_paged_decode(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host
     ws_ptr = _ptr(workspace)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib.astr_paged_decode(ctypes.byref(a), ws_ptr, ws_bytes, _stream_handle(stream)))
+    del keep
+
+
+def astr_paged_decode_noalloc(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host, o, *, sm_scale,
+                              req_to_token_stride, lse=None, num_splits=0, stream=None, mask=None, page_size=1):
+    """Allocation-free paged GQA decode: as astr_paged_decode, with the split partials in the
+    library's fixed device scratch array instead of a caller workspace (no workspace argument)."""
+    lib = load_library()
+    a, keep = make_args(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host, o, sm_scale=sm_scale,
+                        req_to_token_stride=req_to_token_stride, lse=lse, num_splits=num_splits, mask=mask,
+                        page_size=page_size)
+    _check(lib.astr_paged_decode_noalloc(ctypes.byref(a), _stream_handle(stream)))
     del keep
 
 

@@ -317,7 +317,7 @@ int validate_new_kv(const astr_new_kv* nkv) {
 
 // Decode, optionally with the fused append of one new token per request.
 int astr::decode_impl(const astr_paged_args* a, const astr_new_kv* nkv, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+                      void* stream, bool use_scratch) {
   int64_t total = 0;
   int st = validate_common(a, false, &total);
   if (st != ASTR_OK) return st;
@@ -338,6 +338,17 @@ int astr::decode_impl(const astr_paged_args* a, const astr_new_kv* nkv, void* wo
   astr_decode_plan plan;
   st = plan_decode_impl(a, total, num_cus, &plan);
   if (st != ASTR_OK) return st;
+  if (use_scratch) {
+    if (plan.workspace_bytes > (int64_t)ASTR_NOALLOC_SCRATCH_BYTES)
+      return fail(ASTR_ERR_WORKSPACE,
+                  "the plan needs %lld bytes of split partials (batch %d, %d query heads, head_dim %d, %d work groups "
+                  "per kv head), more than the %lld-byte scratch of the allocation-free entry point; call "
+                  "astr_paged_decode with a caller workspace instead",
+                  (long long)plan.workspace_bytes, a->batch, a->num_qo_heads, a->head_dim, plan.num_splits,
+                  (long long)ASTR_NOALLOC_SCRATCH_BYTES);
+    const hipError_t se = astr::scratch_buffer(&workspace, &workspace_bytes);
+    if (se != hipSuccess) return fail(ASTR_ERR_HIP, "scratch address (hipGetSymbolAddress): %s", hipGetErrorString(se));
+  }
   if (workspace == nullptr) return fail(ASTR_ERR_WORKSPACE, "decode needs a workspace of %lld bytes", (long long)plan.workspace_bytes);
   if (!aligned16(workspace)) return fail(ASTR_ERR_WORKSPACE, "workspace must be 16-byte aligned");
   if ((int64_t)workspace_bytes < plan.workspace_bytes)
@@ -396,6 +407,10 @@ extern "C" {
 
 int astr_paged_decode(const astr_paged_args* a, void* workspace, size_t workspace_bytes, void* stream) {
   return astr::decode_impl(a, nullptr, workspace, workspace_bytes, stream);
+}
+
+int astr_paged_decode_noalloc(const astr_paged_args* a, void* stream) {
+  return astr::decode_impl(a, nullptr, nullptr, 0, stream, true);
 }
 
 int astr_paged_decode_append(const astr_paged_args* a, const astr_new_kv* nkv, void* workspace,

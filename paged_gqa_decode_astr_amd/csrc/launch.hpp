@@ -100,6 +100,11 @@ hipError_t launch_decode_combine(const DecodeLaunch& p, hipStream_t stream, cons
 hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream, const Timing& t);
 hipError_t launch_kv_append(const AppendLaunch& p, hipStream_t stream, const Timing& t);
 
+// Device address and size of the library's scratch array on the current
+// device (astr_paged_decode_noalloc's partials); the address is taken once per
+// device with hipGetSymbolAddress and cached.
+hipError_t scratch_buffer(void** out, size_t* bytes);
+
 // Whether a (head_dim, group) pair has a compiled kernel.
 bool decode_supported(int head_dim, int group);
 bool prefill_supported(int head_dim, int group);
