@@ -300,22 +300,62 @@ def main(argv=None):
         pd = tensors.to_device(pin, dev)
         po = torch.empty_like(pd["q"])
         plse = torch.empty(pd["q"].shape[0], pd["q"].shape[1], dtype=torch.float32, device=dev)
-        for _ in range(5):
-            tensors.run_prefill(pd, o=po, lse=plse)
-        torch.cuda.synchronize()
+        pws = tensors.prefill_workspace(pd)          # zeroed once; every call leaves its counters at zero
         psteps = max(10, args.steps // 4)
-        pev = [[HipEvent() for _ in range(2)] for _ in range(psteps)]
-        for k in range(psteps):
-            tensors.run_prefill(pd, o=po, lse=plse, timing_events=pev[k])
-        torch.cuda.synchronize()
-        pms = float(np.mean([e[0].elapsed_time(e[1]) for e in pev]))
         fl = prefill_flops(pin)
-        tf = fl / (pms * 1e-3) / 1e12
+
+        def prefill_us(ws):
+            for _ in range(5):
+                tensors.run_prefill(pd, o=po, lse=plse, workspace=ws)
+            torch.cuda.synchronize()
+            pev = [[HipEvent() for _ in range(2)] for _ in range(psteps)]
+            for k in range(psteps):
+                tensors.run_prefill(pd, o=po, lse=plse, timing_events=pev[k], workspace=ws)
+            torch.cuda.synchronize()
+            return float(np.mean([e[0].elapsed_time(e[1]) for e in pev])) * 1e3
+
+        p_us = prefill_us(pws)
+        whole_us = prefill_us(None)
+        tf = fl / (p_us * 1e-6) / 1e12
+        pa, pkeep = _lib.make_args(pd["q"], pd["k_pool"], pd["v_pool"], pd["req_to_token"], pd["kv_indptr"],
+                                   pd["kv_indptr_host"], po, sm_scale=pd["sm_scale"],
+                                   req_to_token_stride=pd["req_to_token_stride"], qo_indptr=pd["qo_indptr"],
+                                   qo_indptr_host=pd["qo_indptr_host"])
+        pplan = _lib.astr_plan_prefill(pa, 0)
         out["prefill"] = {"workload": f"prefill_b8: {CONFIGS['prefill_b8'].description}",
-                          "us_per_call": round(pms * 1e3, 2), "flops": fl,
+                          "us_per_call": round(p_us, 2), "flops": fl,
+                          "plan": {"work_groups": pplan.num_items, "split_tile_heads": pplan.split_tiles,
+                                   "chunk_key_tiles": pplan.chunk_tiles, "workspace_bytes": pplan.workspace_bytes},
+                          "whole_tiles_us_per_call": round(whole_us, 2),
                           "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
                                        "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
                                        "kernel": f"prefill_kernel<{D},{G}>"}}
+        del pws, pkeep
+        # Long cached prefix with few new tokens (2 requests, 20000 keys, 64 new tokens each): few query
+        # tiles with ~313 key tiles each, where the plan splits the key ranges over the idle CUs.
+        from paged_gqa_decode_astr_amd.workloads import build_paged_inputs
+        lin = build_paged_inputs(np.array([20000, 20000]), 32, 8, 128, 1 << 16, seed=5100, q_lens=np.array([64, 64]))
+        ld = tensors.to_device(lin, dev)
+        lo = torch.empty_like(ld["q"])
+        lws = tensors.prefill_workspace(ld)
+
+        def long_us(ws):
+            for _ in range(3):
+                tensors.run_prefill(ld, o=lo, workspace=ws)
+            torch.cuda.synchronize()
+            ev = [[HipEvent() for _ in range(2)] for _ in range(psteps)]
+            for k in range(psteps):
+                tensors.run_prefill(ld, o=lo, timing_events=ev[k], workspace=ws)
+            torch.cuda.synchronize()
+            return float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
+
+        lsplit, lwhole = long_us(lws), long_us(None)
+        lfl = prefill_flops(lin)
+        out["prefill_long_prefix"] = {
+            "workload": "2 requests, seq_len 20000, q_len 64, Hq 32 / Hkv 8, D 128 (long cached prefix)",
+            "us_per_call_split": round(lsplit, 2), "us_per_call_whole_tiles": round(lwhole, 2),
+            "TFLOPs_split": round(lfl / (lsplit * 1e-6) / 1e12, 1)}
+        del ld, lws
 
     if args.probe:
         log("[bench] probes")

@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define ASTR_ABI_VERSION 5
+#define ASTR_ABI_VERSION 6
 
 /* Default cap on work groups per kv head in an automatic decode plan. */
 #define ASTR_DEFAULT_MAX_SPLITS 256
@@ -213,8 +213,39 @@ int astr_paged_decode(const astr_paged_args* a, void* workspace, size_t workspac
  * and give undefined results; serialise them.  Returns astr_status. */
 int astr_paged_decode_noalloc(const astr_paged_args* a, void* stream);
 
-/* Ragged paged prefill with causal offset seq_len - q_len per request.
- * Needs no workspace (NULL / 0 allowed).  Returns astr_status. */
+/* The automatic prefill plan (no fixed grid: max_q_len == 0, batch <= 96).
+ * Every query tile (128 / G positions x the G heads of one kv head) is one
+ * work group.  When the batch has fewer query tiles than half the device's
+ * work-group slots (e.g. a long cached prefix with few new tokens) and a
+ * workspace is passed, the key range of a tile with more than about
+ * chunk_tiles key tiles (64 keys each) is cut into up to max_chunks (16)
+ * chunks run as separate work groups and merged by the last one to finish, so
+ * that no work group holds many more keys than the balanced share of the CUs.
+ * Other calls (fixed grid, larger batches) keep every tile whole and report
+ * num_items = 0. */
+typedef struct astr_prefill_plan {
+  int32_t num_items;       /* work groups of the call (0: fixed-grid mapping) */
+  int32_t split_tiles;     /* (query tile, kv head) pairs whose key range is split */
+  int32_t chunk_tiles;     /* target key tiles per chunk */
+  int32_t max_chunks;      /* chunk cap per query tile */
+  int64_t partial_bytes;   /* bytes of chunk partials */
+  int64_t workspace_bytes; /* workspace the split plan needs (0: nothing is split) */
+} astr_prefill_plan;
+
+/* Host-only prefill plan (validates a first; no HIP call unless num_cus <= 0,
+ * which asks the current device's CU count).  Returns astr_status. */
+int astr_plan_prefill(const astr_paged_args* a, int32_t num_cus, astr_prefill_plan* out);
+
+/* Ragged paged prefill with causal offset seq_len - q_len per request
+ * ([attention.py @c9ceca1], the commit that batches the torch path with a
+ * causal offset per request in flat qo_indptr order).
+ * workspace: NULL (every query tile runs whole in one work group) or at least
+ * astr_plan_prefill's workspace_bytes, 16-byte aligned, whose contents must be
+ * ZERO before its first use: it holds the split tiles' partials and arrival
+ * counters, and every call leaves the counters at zero again (so one zeroed
+ * workspace serves any number of calls; calls that overlap need distinct
+ * workspaces).  A non-NULL workspace smaller than the plan needs is
+ * ASTR_ERR_WORKSPACE.  Returns astr_status. */
 int astr_paged_prefill(const astr_paged_args* a, void* workspace, size_t workspace_bytes, void* stream);
 
 /* The K and V rows of a step's new tokens, bf16, [rows, Hkv, D]: element

@@ -26,7 +26,7 @@ DEFAULT_MAX_SPLITS = 256
 NOALLOC_SCRATCH_BYTES = 32 << 20   # ASTR_NOALLOC_SCRATCH_BYTES
 
 EXPORTED = ("astr_workspace_size", "astr_plan_decode", "astr_paged_decode", "astr_paged_decode_noalloc",
-            "astr_paged_prefill",
+            "astr_plan_prefill", "astr_paged_prefill",
             "astr_kv_append", "astr_paged_decode_append", "astr_decode_graph_create", "astr_decode_graph_launch",
             "astr_decode_graph_destroy", "astr_last_error", "astr_abi_version")
 
@@ -68,6 +68,11 @@ class DecodePlan(ctypes.Structure):
                 ("grid_y", ctypes.c_int32), ("grid_z", ctypes.c_int32), ("workspace_bytes", ctypes.c_int64)]
 
 
+class PrefillPlan(ctypes.Structure):
+    _fields_ = [("num_items", ctypes.c_int32), ("split_tiles", ctypes.c_int32), ("chunk_tiles", ctypes.c_int32),
+                ("max_chunks", ctypes.c_int32), ("partial_bytes", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
+
+
 _lib = None
 
 
@@ -93,6 +98,8 @@ def load_library(path: str = LIB_PATH):
         f.argtypes = [ctypes.POINTER(PagedArgs), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.astr_paged_decode_noalloc.restype = ctypes.c_int
     lib.astr_paged_decode_noalloc.argtypes = [ctypes.POINTER(PagedArgs), ctypes.c_void_p]
+    lib.astr_plan_prefill.restype = ctypes.c_int
+    lib.astr_plan_prefill.argtypes = [ctypes.POINTER(PagedArgs), ctypes.c_int32, ctypes.POINTER(PrefillPlan)]
     lib.astr_kv_append.restype = ctypes.c_int
     lib.astr_kv_append.argtypes = [ctypes.POINTER(PagedArgs), ctypes.POINTER(NewKV), ctypes.c_void_p]
     lib.astr_paged_decode_append.restype = ctypes.c_int
@@ -250,12 +257,20 @@ def astr_paged_decode_noalloc(q, k_pool, v_pool, req_to_token, kv_indptr, kv_ind
     del keep
 
 
+def astr_plan_prefill(args: PagedArgs, num_cus: int = 0) -> PrefillPlan:
+    plan = PrefillPlan()
+    _check(load_library().astr_plan_prefill(ctypes.byref(args), int(num_cus), ctypes.byref(plan)))
+    return plan
+
+
 def astr_paged_prefill(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host, qo_indptr, qo_indptr_host,
                        o, *, sm_scale, req_to_token_stride, lse=None, max_q_len=0, stream=None,
-                       timing_events=None, non_causal=False, mask=None, page_size=1):
+                       timing_events=None, non_causal=False, mask=None, page_size=1, workspace=None):
     """Ragged paged prefill: q [sum q_len, Hq, D] bf16 in qo_indptr order -> o (+ lse).
 
-    timing_events: optional 2 HipEvent (hip_events.py): start/end stamps of the
+    workspace: None (every query tile whole) or a device tensor of at least astr_plan_prefill's
+    workspace_bytes, zeroed before its first use (long query tiles are then split over several
+    work groups).  timing_events: optional 2 HipEvent (hip_events.py): start/end stamps of the
     prefill kernel."""
     if timing_events is not None and len(timing_events) != 2:
         raise ValueError("prefill timing_events takes 2 events (kernel start/end)")
@@ -264,7 +279,9 @@ def astr_paged_prefill(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_hos
                         req_to_token_stride=req_to_token_stride, lse=lse, qo_indptr=qo_indptr,
                         qo_indptr_host=qo_indptr_host, max_q_len=max_q_len, timing_events=timing_events,
                         non_causal=non_causal, mask=mask, page_size=page_size)
-    _check(lib.astr_paged_prefill(ctypes.byref(a), None, 0, _stream_handle(stream)))
+    ws_ptr = _ptr(workspace)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.astr_paged_prefill(ctypes.byref(a), ws_ptr, ws_bytes, _stream_handle(stream)))
     del keep
 
 

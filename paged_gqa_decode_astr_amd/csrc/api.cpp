@@ -12,6 +12,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -264,6 +265,126 @@ int plan_decode_impl(const astr_paged_args* a, int64_t total_keys, int32_t num_c
   return ASTR_OK;
 }
 
+// Prefill planner constants: key tiles of 64 keys, 128 (position, head) rows
+// per work group, two work groups per CU (one at head_dim 256), chunks of at
+// least kMinChunkTiles key tiles and at most kMaxChunks per query tile.
+constexpr int64_t kPrefillKeyTile = 64;
+constexpr int64_t kPrefillRows = 128;
+#ifndef ASTR_PREFILL_MIN_CHUNK_TILES
+#define ASTR_PREFILL_MIN_CHUNK_TILES 8
+#endif
+#ifndef ASTR_PREFILL_CHUNK_PCT
+#define ASTR_PREFILL_CHUNK_PCT 100
+#endif
+constexpr int64_t kMinChunkTiles = ASTR_PREFILL_MIN_CHUNK_TILES;
+constexpr int64_t kChunkPct = ASTR_PREFILL_CHUNK_PCT;   // chunk length as a percentage of the balanced share
+constexpr int32_t kMaxChunks = astr::kPrefillMaxChunks;
+int64_t prefill_wg_per_cu(int32_t head_dim) { return head_dim == 256 ? 1 : 2; }
+
+// Key tiles of query tile qt of a request (q_len qb, seq_len L).
+int64_t prefill_tile_keys(int64_t qt, int64_t BQ, int64_t qb, int64_t L, bool non_causal) {
+  const int64_t kv_end = non_causal ? L : L - qb + std::min(BQ * (qt + 1), qb);
+  return ceil_div(kv_end, kPrefillKeyTile);
+}
+
+// The automatic prefill plan: the work list (request order, item prefixes)
+// and the chunking.  Lengths come from the host copies, already validated
+// (1 <= q_len <= seq_len).  split = false keeps every tile whole.
+void plan_prefill_impl(const astr_paged_args* a, int32_t num_cus, bool split, astr::PrefillWork* w,
+                       astr_prefill_plan* out) {
+  memset(out, 0, sizeof(*out));
+  w->num_reqs = 0;
+  const int32_t B = a->batch;
+  const int64_t G = a->num_qo_heads / a->num_kv_heads;
+  const int64_t BQ = kPrefillRows / G;
+  const bool nc = a->non_causal != 0;
+  const int32_t* qo = a->qo_indptr_host;
+  const int32_t* kv = a->kv_indptr_host;
+  std::vector<int64_t> work(B), biggest(B);
+  int64_t total = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t qb = qo[b + 1] - qo[b], L = kv[b + 1] - kv[b];
+    int64_t wsum = 0;
+    for (int64_t qt = 0; qt * BQ < qb; ++qt) wsum += prefill_tile_keys(qt, BQ, qb, L, nc);
+    work[b] = wsum;
+    total += wsum * a->num_kv_heads;
+  }
+  const int64_t slots = prefill_wg_per_cu(a->head_dim) * (int64_t)(num_cus > 0 ? num_cus : 1);
+  const int64_t T = std::max<int64_t>(kMinChunkTiles, ceil_div(ceil_div(total, slots) * kChunkPct, 100));
+  w->chunk_tiles = (int32_t)std::min<int64_t>(T, INT32_MAX);
+  // Splitting pays only while whole tiles leave most work-group slots idle:
+  // a CU that holds two work groups already processes key tiles at its full
+  // rate (measured: 2.25 us per 64-key tile per work group at two per CU, about
+  // the rate of one work group alone), so with more whole tiles than half the
+  // slots a split only adds partial traffic and merges.
+  int64_t whole_items = 0;
+  for (int32_t b = 0; b < B; ++b) whole_items += ceil_div((int64_t)qo[b + 1] - qo[b], BQ) * a->num_kv_heads;
+  w->max_chunks = split && 2 * whole_items < slots ? kMaxChunks : 1;
+  w->slices = a->num_kv_heads % 8 == 0 ? 8 : 1;
+  const int64_t hs = a->num_kv_heads / w->slices;
+  // A request's biggest work item (key tiles of its longest chunk; its last
+  // query tile has the most keys).
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t qb = qo[b + 1] - qo[b], L = kv[b + 1] - kv[b];
+    const int64_t nt = prefill_tile_keys(ceil_div(qb, BQ) - 1, BQ, qb, L, nc);
+    const int64_t ns = std::min<int64_t>(w->max_chunks, ceil_div(nt, w->chunk_tiles));
+    biggest[b] = ceil_div(nt, ns);
+  }
+  // Requests whose items are biggest first, then by total work (an
+  // approximately longest-first dispatch order; inside a request the items
+  // already come biggest first).
+  std::vector<int32_t> order(B);
+  for (int32_t b = 0; b < B; ++b) order[b] = b;
+  std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
+    return biggest[x] != biggest[y] ? biggest[x] > biggest[y] : work[x] > work[y];
+  });
+  int64_t first = 0, split_first = 0, split_tiles = 0;
+  for (int32_t r = 0; r < B; ++r) {
+    const int32_t b = order[r];
+    const int64_t qb = qo[b + 1] - qo[b], L = kv[b + 1] - kv[b];
+    int64_t n_g = 0, nsp_g = 0;
+    for (int64_t qt = 0; qt * BQ < qb; ++qt) {
+      const int64_t nt = prefill_tile_keys(qt, BQ, qb, L, nc);
+      const int64_t ns = std::min<int64_t>(w->max_chunks, ceil_div(nt, w->chunk_tiles));
+      n_g += ns;
+      if (ns > 1) {
+        nsp_g += ns;
+        ++split_tiles;
+      }
+    }
+    astr::PrefillWorkReq& q = w->req[r];
+    q.b = b;
+    q.first = (int32_t)first;
+    q.split_first = (int32_t)split_first;
+    q.q0 = qo[b];
+    q.q_len = (int32_t)qb;
+    q.kv0 = kv[b];
+    q.seq_len = (int32_t)L;
+    first += hs * n_g;
+    split_first += hs * nsp_g;
+  }
+  w->req[B] = astr::PrefillWorkReq{0, (int32_t)first, (int32_t)split_first, 0, 0, 0, 0};
+  w->num_reqs = B;
+  const int64_t split_slots = w->slices * split_first;
+  out->num_items = (int32_t)(w->slices * first);
+  out->split_tiles = (int32_t)(split_tiles * a->num_kv_heads);
+  out->chunk_tiles = w->chunk_tiles;
+  out->max_chunks = w->max_chunks;
+  out->partial_bytes = split_slots * astr::prefill_partial_bytes(a->head_dim);
+  out->workspace_bytes = split_slots > 0 ? align256(out->partial_bytes) + split_slots * 4 : 0;
+}
+
+// Whether a prefill call can take the work-list path (automatic plan, batch
+// within the kernel-argument list, item counts within int32).
+bool prefill_work_list_ok(const astr_paged_args* a) {
+  if (a->max_q_len != 0 || a->batch < 1 || a->batch > astr::kMaxWorkReqs) return false;
+  const int64_t BQ = kPrefillRows / (a->num_qo_heads / a->num_kv_heads);
+  int64_t items = 0;
+  for (int32_t b = 0; b < a->batch; ++b)
+    items += ceil_div((int64_t)a->qo_indptr_host[b + 1] - a->qo_indptr_host[b], BQ) * kMaxChunks;
+  return items * a->num_kv_heads < (int64_t(1) << 30);
+}
+
 }  // namespace
 
 extern "C" {
@@ -495,13 +616,18 @@ int astr_kv_append(const astr_paged_args* a, const astr_new_kv* nkv, void* strea
   return ok();
 }
 
-int astr_paged_prefill(const astr_paged_args* a, void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
+}  // extern "C"
+
+namespace {
+
+// Prefill validation (everything but the workspace); *max_q receives the grid's
+// query length (max q_len, or max_q_len when fixed).
+int validate_prefill(const astr_paged_args* a, int32_t* max_q_out) {
   int64_t total = 0;
   int st = validate_common(a, true, &total);
   if (st != ASTR_OK) return st;
-  if (a->batch == 0) return ok();
+  *max_q_out = 0;
+  if (a->batch == 0) return ASTR_OK;
   if (a->qo_indptr == nullptr || a->qo_indptr_host == nullptr)
     return fail(ASTR_ERR_INVALID_ARG, "prefill needs qo_indptr and qo_indptr_host");
   if (a->max_q_len < 0) return fail(ASTR_ERR_INVALID_ARG, "max_q_len must be >= 0");
@@ -524,8 +650,64 @@ int astr_paged_prefill(const astr_paged_args* a, void* workspace, size_t workspa
       return fail(ASTR_ERR_INVALID_ARG, "a q_len of %d exceeds max_q_len %d", max_q, a->max_q_len);
     max_q = a->max_q_len;
   }
+  *max_q_out = max_q;
+  return ASTR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int astr_plan_prefill(const astr_paged_args* a, int32_t num_cus, astr_prefill_plan* out) {
+  if (out == nullptr) return fail(ASTR_ERR_INVALID_ARG, "plan output is NULL");
+  memset(out, 0, sizeof(*out));
+  int32_t max_q = 0;
+  int st = validate_prefill(a, &max_q);
+  if (st != ASTR_OK) return st;
+  if (!prefill_work_list_ok(a)) return ok();
+  if (num_cus <= 0) {
+    st = device_cu_count(&num_cus);
+    if (st != ASTR_OK) return st;
+  }
+  static thread_local astr::PrefillWork w;
+  plan_prefill_impl(a, num_cus, true, &w, out);
+  return ok();
+}
+
+int astr_paged_prefill(const astr_paged_args* a, void* workspace, size_t workspace_bytes, void* stream) {
+  int32_t max_q = 0;
+  int st = validate_prefill(a, &max_q);
+  if (st != ASTR_OK) return st;
+  if (a->batch == 0) return ok();
 
   astr::PrefillLaunch p;
+  memset(&p.work, 0, sizeof(p.work));
+  p.part = nullptr;
+  p.cnt = nullptr;
+  p.part_bytes = 0;
+  if (prefill_work_list_ok(a)) {
+    int num_cus = 0;
+    st = device_cu_count(&num_cus);
+    if (st != ASTR_OK) return st;
+    astr_prefill_plan plan;
+    plan_prefill_impl(a, num_cus, workspace != nullptr, &p.work, &plan);
+    if (plan.workspace_bytes > 0) {
+      if (!aligned16(workspace)) return fail(ASTR_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+      if ((int64_t)workspace_bytes < plan.workspace_bytes)
+        return fail(ASTR_ERR_WORKSPACE,
+                    "prefill workspace of %zu bytes is smaller than the %lld bytes its split plan needs "
+                    "(pass NULL to keep every query tile whole)",
+                    workspace_bytes, (long long)plan.workspace_bytes);
+      if (plan.partial_bytes > (int64_t)UINT32_MAX) {
+        // Beyond one 32-bit buffer range: keep every tile whole.
+        plan_prefill_impl(a, num_cus, false, &p.work, &plan);
+      } else {
+        p.part = static_cast<char*>(workspace);
+        p.cnt = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + align256(plan.partial_bytes));
+        p.part_bytes = (uint32_t)plan.partial_bytes;
+      }
+    }
+  }
   p.batch = a->batch;
   p.num_qo_heads = a->num_qo_heads;
   p.num_kv_heads = a->num_kv_heads;

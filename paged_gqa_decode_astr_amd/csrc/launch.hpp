@@ -60,6 +60,35 @@ struct AppendLaunch {
   int32_t page_shift;         // log2 page size (see DecodeLaunch)
 };
 
+// Work list of an automatic prefill plan, passed by value in the kernel
+// arguments (so a work group knows its request and key range without a
+// round trip to memory).  A query tile's key range is cut into ns
+// near-equal chunks, ns = min(max_chunks, ceil(key tiles / chunk_tiles));
+// each chunk is one work item.  Items are laid out in `slices` interleaved
+// sequences (8 when Hkv is a multiple of 8: block i runs on accelerator die
+// i % 8 and slice i % 8 holds kv heads g = i % 8 + 8 k, so every item of one
+// (request, kv head) group shares that die's L2; otherwise 1).  Inside a
+// slice, requests follow req[0 .. num_reqs) and each request holds, for
+// each of its kv heads in the slice, the group's items: query tiles from the
+// last (most keys) down, chunks of a tile consecutive.  The tiles that are
+// split come first in a group, and their chunks own the partial slots.
+constexpr int kMaxWorkReqs = 96;
+constexpr int kPrefillMaxChunks = 16;  // most key chunks per query tile
+struct PrefillWorkReq {
+  int32_t b;            // request index
+  int32_t first;        // items of the slice before this request
+  int32_t split_first;  // split-tile chunks of the slice before this request
+  int32_t q0, q_len;    // qo_indptr[b], q_len_b
+  int32_t kv0, seq_len; // kv_indptr[b], L_b
+};
+struct PrefillWork {
+  int32_t num_reqs;     // 0: no work list (the kernel reads lengths from device memory)
+  int32_t slices;       // 8 or 1
+  int32_t chunk_tiles;  // T (key tiles of 64)
+  int32_t max_chunks;   // 1 = no split
+  PrefillWorkReq req[kMaxWorkReqs + 1];   // entry num_reqs holds the totals (first, split_first)
+};
+
 struct PrefillLaunch {
   int32_t batch, num_qo_heads, num_kv_heads, head_dim, group;
   float sm_scale;
@@ -85,7 +114,22 @@ struct PrefillLaunch {
   int32_t page_shift;    // log2 page size (see DecodeLaunch)
   bool off32;            // 32-bit buffer offsets: pool rows of a kv head within pool_range bytes, slot ids < 2^24
   uint32_t pool_range;   // off32: (num_slots - 1) * kv_stride_slot * 2 + head_dim * 2
+  // Split tiles (work.max_chunks > 1): partial (acc, max, sum) of every chunk
+  // in slot part[split slot] (prefill_partial_bytes(head_dim) each) and one
+  // arrival counter per split tile in cnt[] (zero before the call; the chunk
+  // that arrives last merges the tile and sets it back to zero).
+  char* part;
+  int32_t* cnt;
+  uint32_t part_bytes;   // bytes of the partial area (buffer range)
+  PrefillWork work;
 };
+
+// Bytes of one chunk's partial: per wavefront, row block and d block the
+// lanes' fp32 accumulators, then per wavefront and row block the lanes'
+// (reference max, row sum).  128 rows per work group.
+constexpr int64_t prefill_partial_bytes(int head_dim) {
+  return 4 * 2 * (head_dim / 16) * 64 * 16 + 4 * 2 * 64 * 8;
+}
 
 // Optional events stamped by the dispatch itself at the kernel's start and
 // end (hipExtLaunchKernel), so their difference is the kernel's own duration.

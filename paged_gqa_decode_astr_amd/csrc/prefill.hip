@@ -36,6 +36,21 @@
 //     order.
 // Output rows are normalised by the row sum and written as bf16 (round to
 // nearest even); lse = reference + log2(sum), returned in natural-log units.
+//
+// Split key ranges (automatic plan with a workspace): the query tiles with the
+// most keys bound the kernel's time (every work group of a batch like
+// prefill_b8 is resident at once, and the tiles of long cached prefixes see
+// up to ~6x the keys of the short ones), so the host cuts each tile's key
+// tiles into ns near-equal chunks of about chunk_tiles and runs each chunk as
+// its own work group.  A chunk leaves its unnormalised accumulators, reference
+// max and row sums in a workspace slot (written, then released at agent
+// scope) and counts itself on the tile's arrival counter; the chunk that
+// arrives last reads the other chunks' slots with agent-coherent loads,
+// merges them with its own registers by the log-sum-exp rule and writes the
+// tile's rows.  Nothing waits on another work group.  The host passes the
+// work list (request order, per-request item prefixes and lengths) in the
+// kernel arguments, so a work group knows its request, tile and key range
+// before its first memory access.
 #include "device_common.hpp"
 #include "kernel_launch.hpp"
 
@@ -69,6 +84,11 @@ struct PShape {
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+// Cache-policy operand of a buffer access: sc1 = coherent at agent scope
+// (the loads see what other work groups released at agent scope, on any XCD).
+constexpr int kScopeAgent = 16;
 
 // Waves per SIMD: two up to head_dim 128; at 256 the accumulators and
 // operands of a wavefront's 32 rows need the whole register file (one wave,
@@ -76,12 +96,32 @@ typedef __attribute__((address_space(3))) void lds_void;
 template <int D>
 constexpr int prefill_waves_per_simd() { return D == 256 ? 1 : 2; }
 
-template <int D, int G, bool OFF32, bool MASK>
+// The (query tile, chunk) a work group runs and its key tiles [it_lo, it_hi).
+struct PrefillItem {
+  int b, g, qt;
+  int q0, qb, kv0, L;
+  int s, ns;             // chunk s of ns (ns == 1: the whole tile)
+  int it_lo, it_hi;
+  int slot, tile_slot;   // split tiles: this chunk's partial slot, the tile's counter (its chunk 0's slot)
+};
+
+// Key tiles of query tile qt (all rows of it) and their chunk count.
+__device__ __forceinline__ int tile_key_tiles(int qt, int BQ, int qb, int L, bool non_causal) {
+  const int kv_end = non_causal ? L : L - qb + min(BQ * (qt + 1), qb);
+  return (kv_end + KT - 1) / KT;
+}
+__device__ __forceinline__ int tile_chunks(int nt, const PrefillWork& w) {
+  return min(w.max_chunks, (nt + w.chunk_tiles - 1) / w.chunk_tiles);
+}
+
+template <int D, int G, bool OFF32, bool MASK, bool WORK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefill_waves_per_simd<D>()))) void prefill_kernel(const PrefillLaunch p) {
   using S = PShape<D>;
   constexpr int BQ = kRows / G;   // query positions per work group
   constexpr int NS = S::kSteps;
   constexpr int NB = S::kDBlocks;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
   // Two stages, each its own array, so that the compiler can tell the LDS
   // DMA into one stage from the reads of the other.
   __shared__ __align__(16) uint16_t sK0[KT * D];
@@ -89,37 +129,92 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefil
   __shared__ __align__(16) uint16_t sV0[KT * D];
   __shared__ __align__(16) uint16_t sV1[KT * D];
 
-  // Work item of this work group.  Consecutive work groups are dealt to the
-  // 8 XCDs in turn, and each XCD has its own L2, so the linear id is remapped
-  // to keep every query tile of one (kv head, request) group on one XCD: the
-  // group's K/V tiles then come from HBM once and from that L2 for the other
-  // query tiles.  Groups are spread over the XCDs round robin, and within a
-  // group the tiles with the most keys start first.
-  const int nq = p.max_q_len > 0 ? (p.max_q_len + BQ - 1) / BQ : 0;
-  const int ngroups = p.num_kv_heads * p.batch;
-  if (nq == 0) return;
-  const int xcd = blockIdx.x % kXcds;
-  const int j = blockIdx.x / kXcds;
-  const int grp = xcd + kXcds * (j / nq);
-  if (grp >= ngroups) return;  // padding of the last round; uniform
-  const int qt = nq - 1 - j % nq;
-  const int g = grp % p.num_kv_heads;
-  const int b = grp / p.num_kv_heads;
-  const int q0 = p.qo_indptr[b];
-  const int qb = p.qo_indptr[b + 1] - q0;
+  PrefillItem it;
+  if constexpr (WORK) {
+    // Work list in the kernel arguments: slice x = blockIdx % slices, position
+    // j = blockIdx / slices in it; the request holding j is the number of
+    // requests after the first whose item prefix is <= j (a ballot over the
+    // prefixes, two per lane).
+    const PrefillWork& w = p.work;
+    const int S_ = w.slices;
+    const int x = blockIdx.x % S_;
+    const int j = blockIdx.x / S_;
+    static_assert(kMaxWorkReqs <= 2 * kWave, "two prefixes per lane");
+    int cnt = 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int i = 1 + lane + kWave * h;
+      const int f = w.req[min(i, kMaxWorkReqs)].first;   // in bounds for every lane
+      cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(i < w.num_reqs && f <= j));
+    }
+    const int r = __builtin_amdgcn_readfirstlane(cnt);
+    const PrefillWorkReq rq = w.req[r];
+    const int hs = p.num_kv_heads / S_;                           // kv heads of the request in this slice
+    const int n_g = (w.req[r + 1].first - rq.first) / hs;         // items of one (request, kv head) group
+    const int nsp_g = (w.req[r + 1].split_first - rq.split_first) / hs;   // of which chunks of split tiles
+    const int local = j - rq.first;
+    const int gi = local / n_g;
+    const int k = local - gi * n_g;
+    it.b = rq.b;
+    it.g = x + S_ * gi;
+    it.q0 = rq.q0;
+    it.qb = rq.q_len;
+    it.kv0 = rq.kv0;
+    it.L = rq.seq_len;
+    // Walk the group's tiles from the last one down to the k-th item.
+    int qt = (it.qb + BQ - 1) / BQ - 1;
+    int before = 0, nt = 0, ns = 1;
+    for (;; --qt) {
+      nt = tile_key_tiles(qt, BQ, it.qb, it.L, p.non_causal);
+      ns = tile_chunks(nt, w);
+      if (k < before + ns || qt == 0) break;
+      before += ns;
+    }
+    it.qt = qt;
+    it.s = k - before;
+    it.ns = ns;
+    it.it_lo = nt * it.s / ns;
+    it.it_hi = nt * (it.s + 1) / ns;
+    const int split_base = rq.split_first + gi * nsp_g;
+    it.slot = (split_base + k) * S_ + x;
+    it.tile_slot = (split_base + before) * S_ + x;
+  } else {
+    // Fixed grid (lengths from device memory).  Consecutive work groups are
+    // dealt to the 8 XCDs in turn, and each XCD has its own L2, so the linear
+    // id is remapped to keep every query tile of one (kv head, request) group
+    // on one XCD: the group's K/V tiles then come from HBM once and from that
+    // L2 for the other query tiles.  Groups are spread over the XCDs round
+    // robin, and within a group the tiles with the most keys start first.
+    const int nq = p.max_q_len > 0 ? (p.max_q_len + BQ - 1) / BQ : 0;
+    const int ngroups = p.num_kv_heads * p.batch;
+    if (nq == 0) return;
+    const int xcd = blockIdx.x % kXcds;
+    const int j = blockIdx.x / kXcds;
+    const int grp = xcd + kXcds * (j / nq);
+    if (grp >= ngroups) return;  // padding of the last round; uniform
+    it.qt = nq - 1 - j % nq;
+    it.g = grp % p.num_kv_heads;
+    it.b = grp / p.num_kv_heads;
+    it.q0 = p.qo_indptr[it.b];
+    it.qb = p.qo_indptr[it.b + 1] - it.q0;
+    if (it.qt * BQ >= it.qb) return;  // uniform over the work group
+    it.kv0 = p.kv_indptr[it.b];
+    it.L = p.kv_indptr[it.b + 1] - it.kv0;
+    it.s = 0;
+    it.ns = 1;
+    it.it_lo = 0;
+    it.it_hi = tile_key_tiles(it.qt, BQ, it.qb, it.L, p.non_causal);
+    it.slot = it.tile_slot = 0;
+  }
+  const int b = it.b, g = it.g, qt = it.qt, q0 = it.q0, qb = it.qb, L = it.L;
   const int p0 = qt * BQ;
-  if (p0 >= qb) return;  // uniform over the work group
-  const int kv0 = p.kv_indptr[b];
-  const int L = p.kv_indptr[b + 1] - kv0;
   const int cofs = L - qb;              // absolute position of query row 0
   const int npos = min(BQ, qb - p0);    // valid positions in this tile
   // Keys [0, kv_end) are visible to some row (all L keys when non-causal).
   const int kv_end = p.non_causal ? L : cofs + p0 + npos;
-  const int ntiles = (kv_end + KT - 1) / KT;
-  const int32_t* ids = p.req_to_token + (p.req_to_token_stride > 0 ? (int64_t)b * p.req_to_token_stride : (int64_t)kv0);
+  const int it_lo = it.it_lo, it_hi = it.it_hi;
+  const int32_t* ids = p.req_to_token + (p.req_to_token_stride > 0 ? (int64_t)b * p.req_to_token_stride : (int64_t)it.kv0);
 
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
   const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int l16 = lane & 15;
   const int kb = lane >> 4;
@@ -190,10 +285,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefil
     __syncthreads();
   };
 
-  // Tile 0 into stage 0, tile 1's slot ids behind it.
-  load_ids(0);
-  gather(sK0, sV0, 0);
-  load_ids(KT);
+  // The first tile of the range into stage 0, the next tile's slot ids behind it.
+  load_ids(it_lo * KT);
+  gather(sK0, sV0, it_lo * KT);
+  load_ids((it_lo + 1) * KT);
 
   // B operand of S^T = K Q^T: lane (r + 16 kb) holds Q[row r][32 ks + 8 kb .. +7] of each row block.
   bf16x8 qop[2][NS];
@@ -233,7 +328,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefil
                                             (int)p.mask_stride_req, 0x00020000);
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) mrow[rb] = (uint32_t)((p0 + (32 * wv + 16 * rb + l16) / G) * p.mask_stride_row);
-    load_mask(0, mcur);
+    load_mask(it_lo * KT, mcur);
   }
   const float qk_scale = p.sm_scale * kLog2e;
   const int lim_min = p.non_causal ? L - 1 : cofs + p0;   // smallest row limit of the work group
@@ -258,7 +353,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefil
   auto tile = [&](auto masked, auto stage, int it) __attribute__((always_inline)) {
     {
       const int t0 = it * KT;
-      const bool more = it + 1 < ntiles;   // uniform
+      const bool more = it + 1 < it_hi;   // uniform
       if (more) {
         if constexpr (decltype(stage)::value == 0) gather(sK1, sV1, t0 + KT); else gather(sK0, sV0, t0 + KT);
         load_ids(t0 + 2 * KT);
@@ -398,24 +493,94 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefil
   };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
-  // Tile it lives in stage it % 2.
+  // Tile it lives in stage (it - it_lo) % 2.
   auto run_tiles = [&](auto masked, int it_begin, int it_end) {
     int it = it_begin;
-    if (it < it_end && (it & 1)) tile(masked, S1{}, it++);
+    if (it < it_end && ((it - it_lo) & 1)) tile(masked, S1{}, it++);
     for (; it + 1 < it_end; it += 2) {
       tile(masked, S0{}, it);
       tile(masked, S1{}, it + 1);
     }
     if (it < it_end) tile(masked, S0{}, it);
   };
-  const int it_plain = MASK ? 0 : min(ntiles, (lim_min + 1) / KT);
-  run_tiles(std::false_type{}, 0, it_plain);
-  run_tiles(std::true_type{}, it_plain, ntiles);
+  const int it_plain = MASK ? it_lo : max(it_lo, min(it_hi, (lim_min + 1) / KT));
+  run_tiles(std::false_type{}, it_lo, it_plain);
+  run_tiles(std::true_type{}, it_plain, it_hi);
 
   // acc[rb][db][q] = O^T[d = 16 db + 4 kb + q][row 16 rb + l16], relative to mref.
+  float ltot[2] = {lacc[0][0], lacc[1][0]};
+  if (WORK && it.ns > 1) {
+    // Split tile: leave this chunk's state in its slot (lane-major, so every
+    // access is one contiguous 1 KB per instruction) with agent-coherent
+    // (sc1, write-through) stores, wait until every one has completed, then
+    // count the chunk on the tile's counter.  (An agent-scope release fence
+    // would also write back the whole L2 of the XCD, which measured 2x slower
+    // for the kernel; the stores that must be seen are all coherent already.)
+    const uint32_t slot_off = (uint32_t)it.slot * (uint32_t)prefill_partial_bytes(D);
+    const uint32_t ml_off = 4u * 2u * NB * kWave * 16u;
+    __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(p.part, (short)0, (int)p.part_bytes, 0x00020000);
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+      for (int db = 0; db < NB; ++db)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[rb][db]), prs,
+                                               slot_off + 16u * (((wv * 2 + rb) * NB + db) * kWave + lane), 0,
+                                               kScopeAgent);
+      const float2 ml = make_float2(mref[rb], ltot[rb]);
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ml), prs,
+                                            slot_off + ml_off + 8u * ((wv * 2 + rb) * kWave + lane), 0, kScopeAgent);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wavefront's slot stores have completed
+    // The arrival count is broadcast through the first word of a K stage,
+    // free since the last tile's barrier (a separate __shared__ word would
+    // take the work group past 64 KB of LDS, and two of them would then no
+    // longer fit on one CU: measured one work group per CU).
+    int* s_arrival = reinterpret_cast<int*>(sK0);
+    __syncthreads();
+    if (tid == 0) *s_arrival = __hip_atomic_fetch_add(p.cnt + it.tile_slot, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (*s_arrival != it.ns - 1) return;   // uniform: another chunk of the tile arrives later and merges
+    // The last chunk: every chunk's slot is complete (its own too).  Read
+    // them with agent-scope (sc1) loads and fold them in chunk order by the
+    // log-sum-exp rule, so the result does not depend on which chunk arrived
+    // last; then reset the counter for the next call.
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      mref[rb] = -INFINITY;
+      ltot[rb] = 0.f;
+#pragma unroll
+      for (int db = 0; db < NB; ++db) acc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int s2 = 0; s2 < it.ns; ++s2) {
+      const uint32_t o2 = (uint32_t)(it.tile_slot + s2 * p.work.slices) * (uint32_t)prefill_partial_bytes(D);
+      float2 ml2[2];
+      f32x4 a2[2][NB];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        ml2[rb] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                 prs, o2 + ml_off + 8u * ((wv * 2 + rb) * kWave + lane), 0, kScopeAgent));
+#pragma unroll
+        for (int db = 0; db < NB; ++db)
+          a2[rb][db] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                     prs, o2 + 16u * (((wv * 2 + rb) * NB + db) * kWave + lane), 0, kScopeAgent));
+      }
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        // A chunk with no visible key for the row has max -inf and sum 0.
+        const float mnew = fmaxf(mref[rb], ml2[rb].x);
+        const float c1 = mref[rb] == -INFINITY ? 0.f : exp2f(mref[rb] - mnew);
+        const float c2 = ml2[rb].x == -INFINITY ? 0.f : exp2f(ml2[rb].x - mnew);
+        ltot[rb] = ltot[rb] * c1 + ml2[rb].y * c2;
+#pragma unroll
+        for (int db = 0; db < NB; ++db) acc[rb][db] = acc[rb][db] * c1 + a2[rb][db] * c2;
+        mref[rb] = mnew;
+      }
+    }
+    if (tid == 0) __hip_atomic_store(p.cnt + it.tile_slot, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
-    const float ltot = lacc[rb][0];
     const int R = 32 * wv + 16 * rb + l16;
     const int posl = R / G;
     if (posl >= npos) continue;
@@ -423,7 +588,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefil
     const int head = g * G + R % G;
     // A row with no visible key (only possible with a mask) is written as
     // zeros with lse = -inf.
-    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    const float inv = ltot[rb] > 0.f ? 1.f / ltot[rb] : 0.f;
     uint16_t* orow = p.o + (int64_t)row * p.o_stride_tok + (int64_t)head * p.o_stride_head;
 #pragma unroll
     for (int db = 0; db < NB; ++db) {
@@ -432,24 +597,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefil
       *reinterpret_cast<uint2*>(orow + 16 * db + 4 * kb) = make_uint2(w0, w1);
     }
     if (p.lse != nullptr && kb == 0)
-      p.lse[(int64_t)row * p.lse_stride_tok + head] = ltot > 0.f ? (mref[rb] + log2f(ltot)) * kLn2 : -INFINITY;
+      p.lse[(int64_t)row * p.lse_stride_tok + head] = ltot[rb] > 0.f ? (mref[rb] + log2f(ltot[rb])) * kLn2 : -INFINITY;
   }
+}
+
+template <int D, int G, bool WORK>
+hipError_t launch_w(const PrefillLaunch& p, dim3 grid, hipStream_t s, const Timing& t) {
+  if (p.mask != nullptr) {
+    if (p.off32) return launch_kernel(prefill_kernel<D, G, true, true, WORK>, grid, dim3(kThreads), s, t, p);
+    return launch_kernel(prefill_kernel<D, G, false, true, WORK>, grid, dim3(kThreads), s, t, p);
+  }
+  if (p.off32) return launch_kernel(prefill_kernel<D, G, true, false, WORK>, grid, dim3(kThreads), s, t, p);
+  return launch_kernel(prefill_kernel<D, G, false, false, WORK>, grid, dim3(kThreads), s, t, p);
 }
 
 template <int D, int G>
 hipError_t launch_t(const PrefillLaunch& p, hipStream_t s, const Timing& t) {
+  if (p.work.num_reqs > 0) {
+    // One work group per item of the work list.
+    const int64_t blocks = (int64_t)p.work.slices * p.work.req[p.work.num_reqs].first;
+    if (blocks < 1 || blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    return launch_w<D, G, true>(p, dim3((unsigned)blocks, 1, 1), s, t);
+  }
   constexpr int BQ = kRows / G;
   const int64_t nq = (p.max_q_len + BQ - 1) / BQ;
   const int64_t groups = (int64_t)p.num_kv_heads * p.batch;
   const int64_t blocks = kXcds * ((groups + kXcds - 1) / kXcds) * nq;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  const dim3 grid((unsigned)blocks, 1, 1);
-  if (p.mask != nullptr) {
-    if (p.off32) return launch_kernel(prefill_kernel<D, G, true, true>, grid, dim3(kThreads), s, t, p);
-    return launch_kernel(prefill_kernel<D, G, false, true>, grid, dim3(kThreads), s, t, p);
-  }
-  if (p.off32) return launch_kernel(prefill_kernel<D, G, true, false>, grid, dim3(kThreads), s, t, p);
-  return launch_kernel(prefill_kernel<D, G, false, false>, grid, dim3(kThreads), s, t, p);
+  return launch_w<D, G, false>(p, dim3((unsigned)blocks, 1, 1), s, t);
 }
 
 }  // namespace

@@ -85,16 +85,36 @@ def run_decode_append(dev: dict, o=None, lse=None, workspace=None, num_splits=0,
     return o
 
 
+def prefill_workspace(dev: dict, non_causal=False, mask=None, max_q_len=0, device=None):
+    """A zeroed workspace sized by astr_plan_prefill for this batch (None when its plan splits nothing)."""
+    q = dev["q"]
+    a, keep = _lib.make_args(q, dev["k_pool"], dev["v_pool"], dev["req_to_token"], dev["kv_indptr"],
+                             dev["kv_indptr_host"], q, sm_scale=dev["sm_scale"],
+                             req_to_token_stride=dev["req_to_token_stride"], qo_indptr=dev["qo_indptr"],
+                             qo_indptr_host=dev["qo_indptr_host"], max_q_len=max_q_len, non_causal=non_causal,
+                             mask=mask, page_size=dev.get("page_size", 1))
+    nbytes = _lib.astr_plan_prefill(a, 0).workspace_bytes
+    del keep
+    if nbytes == 0:
+        return None
+    return torch.zeros((nbytes + 3) // 4, dtype=torch.int32, device=device or q.device)
+
+
 def run_prefill(dev: dict, o=None, lse=None, max_q_len=0, stream=None, timing_events=None, non_causal=False,
-                mask=None):
+                mask=None, workspace="auto"):
+    """workspace: "auto" (a fresh zeroed workspace from the plan, so long tiles are split), None (every
+    query tile whole) or a zeroed tensor reused across calls."""
     q = dev["q"]
     if o is None:
         o = torch.empty_like(q)
+    if isinstance(workspace, str):
+        workspace = prefill_workspace(dev, non_causal=non_causal, mask=mask, max_q_len=max_q_len)
     _lib.astr_paged_prefill(q, dev["k_pool"], dev["v_pool"], dev["req_to_token"], dev["kv_indptr"],
                             dev["kv_indptr_host"], dev["qo_indptr"], dev["qo_indptr_host"], o,
                             sm_scale=dev["sm_scale"], req_to_token_stride=dev["req_to_token_stride"], lse=lse,
                             max_q_len=max_q_len, stream=stream, timing_events=timing_events,
-                            non_causal=non_causal, mask=mask, page_size=dev.get("page_size", 1))
+                            non_causal=non_causal, mask=mask, page_size=dev.get("page_size", 1),
+                            workspace=workspace)
     return o
 
 
