@@ -174,6 +174,9 @@ typedef struct astr_decode_plan {
 
 /* Workspace bytes a decode call needs for `batch` requests with up to
  * `max_splits` work groups per kv head (0 = ASTR_DEFAULT_MAX_SPLITS).
+ * [extension @6f67ba8], the commit moving the decode split partials
+ * (o_part, ml_part) from per-file cached tensors into a preallocated,
+ * caller-owned workspace. 
  * Layout (both fp32, offsets from the workspace base, P = Wh + B - 1):
  *   o_part  at 0:                          [Hq][P][D]  normalised split output
  *   ml_part at align256(Hq * P * D * 4):   [Hq][P][2]  (max logit m, sum l)
@@ -182,14 +185,19 @@ typedef struct astr_decode_plan {
 size_t astr_workspace_size(int32_t batch, int32_t num_qo_heads, int32_t head_dim, int32_t max_splits);
 
 /* Host-only decode plan (no HIP call): the number of work groups per kv head
- * and the workspace it needs.  num_cus > 0 sets the compute-unit count the
+ * and the workspace it needs.  [extension @6f67ba8], the commit extracting the
+ * shared split-count helper (compute_num_splits) and the partial allocation;
+ * the pages give only its name, the rule here is this library's balanced flat
+ * split (keys of a kv head laid end to end, cut into near-equal ranges).  num_cus > 0 sets the compute-unit count the
  * plan targets; num_cus <= 0 asks the current device.  Needs kv_indptr_host
  * unless a->num_splits > 0.  Returns astr_status. */
 int astr_plan_decode(const astr_paged_args* a, int32_t num_cus, astr_decode_plan* out);
 
-/* Paged GQA decode: one query row per request.  Enqueues the split kernel,
- * which writes partials into `workspace`, then the combine kernel, which
- * writes o (and lse).  workspace_bytes must be >= the plan's workspace_bytes.
+/* Paged GQA decode: one query row per request ([extension @6f67ba8], the
+ * commits wiring paged decode with req_to_token as a page table of page size
+ * one, and turning decode into split-KV partials merged by a separate combine
+ * kernel).  Enqueues the split kernel, which writes partials into
+ * `workspace`, then the combine kernel, which writes o (and lse).  workspace_bytes must be >= the plan's workspace_bytes.
  * Returns astr_status. */
 int astr_paged_decode(const astr_paged_args* a, void* workspace, size_t workspace_bytes, void* stream);
 
@@ -328,10 +336,14 @@ int astr_decode_graph_launch(const astr_decode_graph* graph, void* stream);
 /* Releases the graph (NULL is a no-op). */
 int astr_decode_graph_destroy(astr_decode_graph* graph);
 
-/* Message for the last non-OK status returned on this thread ("" if none). */
+/* Message for the last non-OK status returned on this thread ("" if none).
+ * The pages check every launch through launch-check macros ([backend
+ * @c9ceca1], commits page for astrai/extension/backend at c9ceca1, the entry
+ * adding them); here each status carries its message instead. */
 const char* astr_last_error(void);
 
-/* ASTR_ABI_VERSION of the built library. */
+/* ASTR_ABI_VERSION of the built library (not from the pages: a check that the
+ * header and the loaded library agree). */
 int astr_abi_version(void);
 
 #ifdef __cplusplus

@@ -27,12 +27,14 @@ Parity status of each function is listed in its module header.
 from .attention import (bf16_bits_to_f64, f64_to_bf16_bits, request_slots, paged_attention,
                         attention_over_range)
 from .partition import (DEFAULTS, plan_num_splits, active_groups, wg_bounds, piece_table, pieces_of_request,
-                        split_partials, combine_partials, decode_via_splits)
+                        split_partials, combine_partials, decode_via_splits, PREFILL, prefill_tiles, prefill_plan,
+                        prefill_via_chunks)
 from .kv_append import new_token_slots, kv_append
 
 __all__ = [
     "bf16_bits_to_f64", "f64_to_bf16_bits", "request_slots", "paged_attention",
     "attention_over_range", "DEFAULTS", "plan_num_splits", "active_groups", "wg_bounds", "piece_table",
-    "pieces_of_request", "split_partials", "combine_partials", "decode_via_splits",
+    "pieces_of_request", "split_partials", "combine_partials", "decode_via_splits", "PREFILL", "prefill_tiles",
+    "prefill_plan", "prefill_via_chunks",
     "new_token_slots", "kv_append",
 ]

@@ -38,6 +38,12 @@ piece's keys, l = sum exp(s - m), o = sum exp(s - m) v / l (normalised).
 Merge: M = max m_s, w_s = l_s exp(m_s - M), O = sum w_s o_s / sum w_s,
 lse = M + ln sum w_s.
 
+Prefill split plan (end of this file): pinned in tests/test_oracle.py -- the
+chunked computation equals the definition to 1e-12 for every chunk count (so
+any chunking of a tile's key tiles is a correct result), and the chunks tile
+each query tile's key range exactly; the C++ planner's summary equals
+prefill_plan's exactly (tests/test_abi_cpu.py).
+
 Parity: pinned in tests/test_oracle.py -- the merge of split partials equals
 the direct definition (oracle.attention) to 1e-12 for every split count,
 pieces tile each request exactly, slots are unique, ranges differ by at most
@@ -162,3 +168,103 @@ def decode_via_splits(q_bits, k_pool_bits, v_pool_bits, req_to_token, req_to_tok
     o_part, ml_part = split_partials(q_bits, k_pool_bits, v_pool_bits, req_to_token,
                                      req_to_token_stride, kv_indptr, sm_scale, Wh)
     return combine_partials(o_part, ml_part, kv_indptr, Wh)
+
+
+# ----------------------------------------------------------------------------- prefill split plan
+#
+# Ragged prefill runs one work group per query tile: 128 // G query positions
+# of one request times the G query heads of one kv head.  Query tile qt of
+# request b (q_b new tokens, L_b keys) covers positions [qt*BQ, min((qt+1)*BQ,
+# q_b)); its rows see keys up to (L_b - q_b) + min((qt+1)*BQ, q_b) - 1
+# (all L_b keys when non-causal), i.e. nt = ceil(kv_end / 64) key tiles of 64.
+#
+# This project's split rule (the pages only say that long key ranges are
+# split into partials merged by a combine step, for decode): with S slots
+# (two work groups per CU, one at head_dim 256) and T = max(8, ceil(total
+# key tiles over all (tile, kv head) / S)), a tile is cut into
+# ns = min(16, ceil(nt / T)) chunks, chunk s covering key tiles
+# [floor(nt*s/ns), floor(nt*(s+1)/ns)) -- but only when the whole tiles,
+# times Hkv, number fewer than S / 2 (otherwise every ns is 1).  The plan
+# applies to the automatic grid of at most 96 requests.
+
+PREFILL = {"rows": 128, "key_tile": 64, "min_chunk_tiles": 8, "max_chunks": 16, "max_reqs": 96}
+
+
+def prefill_tiles(qo_indptr, kv_indptr, group, non_causal=False):
+    """[(b, qt, nt)] for every query tile of the batch."""
+    BQ = PREFILL["rows"] // group
+    KT = PREFILL["key_tile"]
+    out = []
+    for b in range(len(kv_indptr) - 1):
+        qb = int(qo_indptr[b + 1] - qo_indptr[b])
+        L = int(kv_indptr[b + 1] - kv_indptr[b])
+        for qt in range(_ceil_div(qb, BQ)):
+            kv_end = L if non_causal else L - qb + min(BQ * (qt + 1), qb)
+            out.append((b, qt, _ceil_div(kv_end, KT)))
+    return out
+
+
+def prefill_plan(qo_indptr, kv_indptr, num_qo_heads, num_kv_heads, head_dim, num_cus, non_causal=False,
+                 split=True):
+    """The split plan's summary (num_items, split_tiles, chunk_tiles, max_chunks, partial_bytes,
+    workspace_bytes) and the chunk count of every query tile {(b, qt): ns}."""
+    B = len(kv_indptr) - 1
+    group = num_qo_heads // num_kv_heads
+    if B < 1 or B > PREFILL["max_reqs"]:
+        return None, {}
+    tiles = prefill_tiles(qo_indptr, kv_indptr, group, non_causal)
+    slots = (1 if head_dim == 256 else 2) * num_cus
+    total = sum(nt for _, _, nt in tiles) * num_kv_heads
+    T = max(PREFILL["min_chunk_tiles"], _ceil_div(total, slots))
+    splitting = split and 2 * len(tiles) * num_kv_heads < slots
+    max_chunks = PREFILL["max_chunks"] if splitting else 1
+    ns = {(b, qt): min(max_chunks, _ceil_div(nt, T)) for b, qt, nt in tiles}
+    items = sum(ns.values()) * num_kv_heads
+    split_chunks = sum(n for n in ns.values() if n > 1) * num_kv_heads
+    split_tiles = sum(1 for n in ns.values() if n > 1) * num_kv_heads
+    part_one = 4 * 2 * (head_dim // 16) * 64 * 16 + 4 * 2 * 64 * 8
+    partial_bytes = split_chunks * part_one
+    ws = (_ceil_div(partial_bytes, 256) * 256 + split_chunks * 4) if split_chunks else 0
+    return {"num_items": items, "split_tiles": split_tiles, "chunk_tiles": T, "max_chunks": max_chunks,
+            "partial_bytes": partial_bytes, "workspace_bytes": ws}, ns
+
+
+def prefill_via_chunks(q_bits, k_pool_bits, v_pool_bits, req_to_token, req_to_token_stride, kv_indptr, qo_indptr,
+                       sm_scale, ns_of, group, non_causal=False):
+    """Prefill computed chunk by chunk: each query tile's key tiles cut as the plan says, each
+    chunk's (m, l, o) partial over its keys, merged by the log-sum-exp rule.  Returns (O, lse)."""
+    BQ = PREFILL["rows"] // group
+    KT = PREFILL["key_tile"]
+    qf = bf16_bits_to_f64(q_bits)
+    kf = bf16_bits_to_f64(k_pool_bits)
+    vf = bf16_bits_to_f64(v_pool_bits)
+    rows, Hq, D = qf.shape
+    Hkv = kf.shape[1]
+    sigma = float(np.float32(sm_scale))
+    O = np.zeros((rows, Hq, D))
+    lse = np.full((rows, Hq), -np.inf)
+    for b, qt, nt in prefill_tiles(qo_indptr, kv_indptr, group, non_causal):
+        q0 = int(qo_indptr[b])
+        qb = int(qo_indptr[b + 1]) - q0
+        L = int(kv_indptr[b + 1] - kv_indptr[b])
+        slots = request_slots(req_to_token, req_to_token_stride, kv_indptr, b)
+        ns = ns_of[(b, qt)]
+        for i in range(qt * BQ, min((qt + 1) * BQ, qb)):
+            last = L - 1 if non_causal else L - qb + i
+            for h in range(Hq):
+                g = h * Hkv // Hq
+                parts = []
+                for s in range(ns):
+                    t0, t1 = (nt * s // ns) * KT, min((nt * (s + 1) // ns) * KT, last + 1)
+                    if t1 <= t0:
+                        continue
+                    keys = slots[t0:t1]
+                    logits = sigma * (kf[keys, g, :] @ qf[q0 + i, h, :])
+                    m = logits.max()
+                    p = np.exp(logits - m)
+                    parts.append((m, p.sum(), p @ vf[keys, g, :] / p.sum()))
+                M = max(m for m, _, _ in parts)
+                w = [l * np.exp(m - M) for m, l, _ in parts]
+                O[q0 + i, h] = sum(wi * o for wi, (_, _, o) in zip(w, parts)) / sum(w)
+                lse[q0 + i, h] = M + np.log(sum(w))
+    return O, lse

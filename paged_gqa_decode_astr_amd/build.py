@@ -1,6 +1,9 @@
 """Build libastr_attn.so in-tree with hipcc for gfx950.
 
-Usage: python -m paged_gqa_decode_astr_amd.build [--jobs N]
+Usage: python -m paged_gqa_decode_astr_amd.build [--jobs N] [--probes]
+
+--probes also builds the standalone measurement programs under probes/ (not
+part of the library; the gather-ceiling probe behind the decode roofline).
 
 Every HIP source is compiled with packed-fp32 instructions disabled; the host
 C++ ABI layer is compiled by the same driver.  Objects go to _build/, the
@@ -94,9 +97,11 @@ def build_probes(verbose: bool = False):
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=None)
+    ap.add_argument("--probes", action="store_true", help="also build the measurement programs in probes/")
     args = ap.parse_args(argv)
     build(args.jobs, verbose=True)
-    build_probes(verbose=True)
+    if args.probes:
+        build_probes(verbose=True)
 
 
 if __name__ == "__main__":

@@ -1,5 +1,5 @@
-// Device helpers for the gfx950 kernels: bf16 unpacking/rounding and
-// wavefront (64-lane) reductions.
+// Device helpers for the gfx950 kernels: bf16 rounding and wavefront
+// (64-lane) reductions.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -11,24 +11,12 @@ constexpr int kWave = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// Low / high bf16 of a 32-bit word, widened exactly to fp32.
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
 // fp32 -> bf16 with round-to-nearest-even; NaN maps to a quiet NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
   u += 0x7fffu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
-}
-
-// Eight bf16 (one 16-byte vector) widened to fp32.
-__device__ __forceinline__ void unpack8(const uint4& v, float (&f)[8]) {
-  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
-  f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
-  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
-  f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
 }
 
 // Butterfly sum / max over lanes whose ids differ only in the bits of

@@ -10,6 +10,10 @@ from paged_gqa_decode_astr_amd import tensors
 ATOL = 1e-2   # max-abs bar against the fp64 oracle
 RTOL = 2e-2   # max-rel bar against the fp64 oracle
 
+# Every assert_close call's measured errors, in call order: (what, max_abs, max_rel over |ref| >= 1e-2,
+# elements).  conftest.py writes them to the file named by ASTR_PARITY_REPORT at the end of a session.
+PARITY_RECORDS = []
+
 
 def announce(msg: str):
     """Name the case before a GPU step, flushed, so a dying run still says what it ran."""
@@ -39,6 +43,8 @@ def assert_close(got: torch.Tensor, ref: np.ndarray, what: str, atol=ATOL, rtol=
     bad = err > atol + rtol * np.abs(ref)
     big = np.abs(ref) >= 1e-2
     max_rel = float((err[big] / np.abs(ref[big])).max()) if big.any() else 0.0
+    PARITY_RECORDS.append({"what": what, "max_abs": float(err.max()), "max_rel": max_rel, "elements": int(err.size),
+                           "atol": atol, "rtol": rtol})
     msg = f"{what}: max_abs={err.max():.3e} max_rel(|ref|>=1e-2)={max_rel:.3e} bad={int(bad.sum())}"
     if bad.any():
         idx = np.unravel_index(np.argmax(err - (atol + rtol * np.abs(ref))), err.shape)

@@ -16,3 +16,15 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def golden_dir():
     return os.path.join(ROOT, "tests", "golden")
+
+
+def pytest_sessionfinish(session, exitstatus):
+    """With ASTR_PARITY_REPORT set, write the measured max-abs / max-rel of every GPU parity check."""
+    path = os.environ.get("ASTR_PARITY_REPORT")
+    helpers = sys.modules.get("_gpu_helpers")
+    if not path or helpers is None or not helpers.PARITY_RECORDS:
+        return
+    import json
+    os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+    with open(path, "w") as fh:
+        json.dump(helpers.PARITY_RECORDS, fh, indent=0)

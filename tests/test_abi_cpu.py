@@ -331,3 +331,63 @@ def test_page_size_validation(ps, stride, kv, needle):
     a.req_to_token_stride = stride
     assert _call_decode(a) == _lib.ASTR_ERR_INVALID_ARG
     assert needle in _lib.astr_last_error()
+
+
+def _prefill_plan_args(qo, kv, Hq=32, Hkv=8, D=128, non_causal=False):
+    a = _lib.PagedArgs()
+    a.batch = len(kv) - 1
+    a.num_qo_heads, a.num_kv_heads, a.head_dim = Hq, Hkv, D
+    a.sm_scale = 0.1
+    kvh = np.ascontiguousarray(kv, dtype=np.int32)
+    qoh = np.ascontiguousarray(qo, dtype=np.int32)
+    dummy = np.zeros(64, dtype=np.uint16)       # host memory: the planner never dereferences device pointers
+    L = np.diff(kvh)
+    a.q = a.o = a.k_pool = a.v_pool = ctypes.c_void_p(((dummy.ctypes.data + 15) // 16) * 16)
+    a.q_stride_tok, a.q_stride_head = Hq * D, D
+    a.o_stride_tok, a.o_stride_head = Hq * D, D
+    a.kv_stride_slot, a.kv_stride_head = Hkv * D, D
+    a.num_slots = int(kvh[-1]) + 1
+    a.req_to_token = a.kv_indptr = a.qo_indptr = ctypes.c_void_p(dummy.ctypes.data)
+    a.req_to_token_stride = int(L.max())
+    a.kv_indptr_host = kvh.ctypes.data_as(ctypes.c_void_p)
+    a.qo_indptr_host = qoh.ctypes.data_as(ctypes.c_void_p)
+    a.non_causal = 1 if non_causal else 0
+    return a, (kvh, qoh, dummy)
+
+
+def test_prefill_plan_matches_oracle_random():
+    """The library's automatic prefill plan equals the oracle's independent statement of it."""
+    rng = np.random.default_rng(77)
+    for _ in range(400):
+        B = int(rng.integers(1, 120))
+        hi = int(rng.choice([50, 2000, 40000]))
+        L = rng.integers(1, hi + 1, size=B)
+        q = np.array([int(rng.integers(1, min(int(x), int(rng.choice([8, 600]))) + 1)) for x in L])
+        kv = np.concatenate([[0], np.cumsum(L)])
+        qo = np.concatenate([[0], np.cumsum(q)])
+        Hkv = int(rng.choice([1, 2, 4, 8, 16]))
+        G = int(rng.choice([1, 2, 4, 8]))
+        D = int(rng.choice([64, 128, 256]))
+        nc = bool(rng.integers(0, 2))
+        cus = int(rng.choice([80, 256, 304]))
+        a, keep = _prefill_plan_args(qo, kv, Hq=Hkv * G, Hkv=Hkv, D=D, non_causal=nc)
+        got = _lib.astr_plan_prefill(a, cus)
+        want, _ = oracle.prefill_plan(qo, kv, Hkv * G, Hkv, D, cus, non_causal=nc)
+        if want is None:
+            assert got.num_items == 0 and got.workspace_bytes == 0, B
+            continue
+        for f in ("num_items", "split_tiles", "chunk_tiles", "max_chunks", "partial_bytes", "workspace_bytes"):
+            assert getattr(got, f) == want[f], (f, getattr(got, f), want[f], B, Hkv, G, D, nc, cus)
+
+
+def test_prefill_plan_examples():
+    # prefill_b8 seed 5000: 448 whole tiles on 256 CUs (>= half of 512 slots): nothing is split.
+    from paged_gqa_decode_astr_amd.workloads import make_inputs
+    inp = make_inputs("prefill_b8", 0)
+    a, keep = _prefill_plan_args(inp["qo_indptr"], inp["kv_indptr"])
+    p = _lib.astr_plan_prefill(a, 256)
+    assert (p.num_items, p.split_tiles, p.workspace_bytes) == (448, 0, 0)
+    # Two 20000-key requests with 64 new tokens: 16 tiles, each cut 16 ways.
+    a, keep = _prefill_plan_args([0, 64, 128], [0, 20000, 40000])
+    p = _lib.astr_plan_prefill(a, 256)
+    assert (p.split_tiles, p.max_chunks, p.num_items) == (32, 16, 512)

@@ -375,3 +375,40 @@ def test_generator_is_deterministic_and_shaped():
     assert L.min() >= 1 and L.max() <= 64 and a["k_pool"].shape == (512, 1, 64)
     used = a["req_to_token"][a["req_to_token"] >= 0]
     assert len(set(used.tolist())) == len(used) == int(L.sum())
+
+
+# ----------------------------------------------------------------------------- prefill chunks
+
+@pytest.mark.parametrize("forced", [1, 2, 3, 7])
+def test_prefill_chunks_merge_to_the_definition(forced):
+    """Cutting every query tile's key tiles into `forced` chunks (partials merged by the
+    log-sum-exp rule) gives the definition's O and lse to 1e-12."""
+    seq = np.array([300, 70, 777, 129])
+    ql = np.array([40, 70, 200, 1])
+    inp = build_paged_inputs(seq, 8, 2, 16, 2048, seed=41, q_lens=ql)
+    ns = {(b, qt): forced for b, qt, _ in oracle.prefill_tiles(inp["qo_indptr"], inp["kv_indptr"], 4)}
+    o, lse = oracle.prefill_via_chunks(inp["q"], inp["k_pool"], inp["v_pool"], inp["req_to_token"],
+                                      inp["req_to_token_stride"], inp["kv_indptr"], inp["qo_indptr"], inp["sm_scale"],
+                                      ns, 4)
+    ref_o, ref_lse = oracle.paged_attention(inp["q"], inp["k_pool"], inp["v_pool"], inp["req_to_token"],
+                                            inp["req_to_token_stride"], inp["kv_indptr"], inp["sm_scale"],
+                                            qo_indptr=inp["qo_indptr"])
+    assert np.abs(o - ref_o).max() < 1e-12
+    assert np.abs(lse - ref_lse).max() < 1e-12
+
+
+def test_prefill_plan_chunks_tile_the_key_range():
+    rng = np.random.default_rng(17)
+    for _ in range(200):
+        B = int(rng.integers(1, 9))
+        L = rng.integers(1, 40000, size=B)
+        q = np.array([int(rng.integers(1, min(int(x), 600) + 1)) for x in L])
+        kv = np.concatenate([[0], np.cumsum(L)])
+        qo = np.concatenate([[0], np.cumsum(q)])
+        summary, ns = oracle.prefill_plan(qo, kv, 32, 8, 128, 256)
+        for (b, qt, nt) in oracle.prefill_tiles(qo, kv, 4):
+            n = ns[(b, qt)]
+            assert 1 <= n <= oracle.PREFILL["max_chunks"]
+            cuts = [nt * s // n for s in range(n + 1)]
+            assert cuts[0] == 0 and cuts[-1] == nt and all(cuts[s + 1] > cuts[s] for s in range(n)), (nt, n)
+        assert summary["num_items"] == sum(ns.values()) * 8
