@@ -328,11 +328,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(split_
       const int jc = min(lane, n - 1);
       const int tb = pt.t_begin(jc), te = pt.t_end(jc);
       const int pairs = lane < n ? (te - tb + 2 * kTile - 1) / (2 * kTile) : 0;
+      // Inclusive scan over the lanes.  The lane id passes through an empty
+      // asm so that the source-lane addresses are formed here, per window,
+      // instead of being hoisted out of the loop as six live registers.
       int x = pairs;
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
 #pragma unroll
       for (int o = 1; o < kWave; o <<= 1) {
-        const int y = __shfl_up(x, o, kWave);
-        if (lane >= o) x += y;
+        const int y = __builtin_amdgcn_ds_bpermute((ln - o) << 2, x);
+        if (ln >= o) x += y;
       }
       incl = x;
       if (lane <= n) tab[lane] = PieceEntry{x - pairs, tb, te, pt.kv[jc]};
@@ -460,7 +465,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(split_
     mA = mask_at(c2);
     load_tile<D, OFF32>(Bt, pv, slot_at(c1, iB), lane);
     if constexpr (MASK) Bt.vis = __builtin_amdgcn_ballot_w64(mB != 0);
-    if (lane == 0) sm_lead[wv] = int4{-1, 0, 0, 0};
+    // No merge led by this wavefront yet (only .x is read before a merge
+    // record overwrites all fields; a one-register constant, so the compiler
+    // does not keep a four-register tuple live across the window).
+    if (lane == 0) sm_lead[wv].x = -1;
     __syncthreads();
 
     float mref = -INFINITY, mx = -INFINITY, lsum = 0.f;
