@@ -67,10 +67,24 @@ def build(jobs: int | None = None, extra=(), verbose: bool = False) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    _check_no_missing_kernels(tmp)
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
     return LIB
+
+
+def _check_no_missing_kernels(lib: str) -> None:
+    """The link succeeds even when the host pass of a source left a kernel's
+    launch stub out (the symbol stays undefined until the library is
+    loaded); catch that here rather than at load time."""
+    res = subprocess.run(["nm", "-D", "--undefined-only", lib], capture_output=True, text=True)
+    if res.returncode != 0:
+        return   # no nm: the load-time check in the binding still applies
+    missing = [ln.split()[-1] for ln in res.stdout.splitlines() if "_ZN4astr" in ln]
+    if missing:
+        os.remove(lib)
+        raise RuntimeError(f"{len(missing)} library symbols left undefined, e.g. {missing[0]}")
 
 
 PROBES = os.path.join(PKG, "probes")

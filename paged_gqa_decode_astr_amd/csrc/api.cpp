@@ -322,13 +322,18 @@ void plan_prefill_impl(const astr_paged_args* a, int32_t num_cus, bool split, as
   w->max_chunks = split && 2 * whole_items < slots ? kMaxChunks : 1;
   w->slices = a->num_kv_heads % 8 == 0 ? 8 : 1;
   const int64_t hs = a->num_kv_heads / w->slices;
-  // A request's biggest work item (key tiles of its longest chunk; its last
-  // query tile has the most keys).
+  // A request's biggest work item: key tiles of its longest chunk or whole
+  // tile.  Not always from the last query tile: a tile just over the chunk
+  // length is cut in two halves, while the tile before it may stay whole.
   for (int32_t b = 0; b < B; ++b) {
     const int64_t qb = qo[b + 1] - qo[b], L = kv[b + 1] - kv[b];
-    const int64_t nt = prefill_tile_keys(ceil_div(qb, BQ) - 1, BQ, qb, L, nc);
-    const int64_t ns = std::min<int64_t>(w->max_chunks, ceil_div(nt, w->chunk_tiles));
-    biggest[b] = ceil_div(nt, ns);
+    int64_t big = 0;
+    for (int64_t qt = 0; qt * BQ < qb; ++qt) {
+      const int64_t nt = prefill_tile_keys(qt, BQ, qb, L, nc);
+      const int64_t ns = std::min<int64_t>(w->max_chunks, ceil_div(nt, w->chunk_tiles));
+      big = std::max(big, ceil_div(nt, ns));
+    }
+    biggest[b] = big;
   }
   // Requests whose items are biggest first, then by total work (an
   // approximately longest-first dispatch order; inside a request the items
