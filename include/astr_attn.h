@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define ASTR_ABI_VERSION 6
+#define ASTR_ABI_VERSION 7
 
 /* Default cap on work groups per kv head in an automatic decode plan. */
 #define ASTR_DEFAULT_MAX_SPLITS 256
@@ -240,6 +240,11 @@ typedef struct astr_prefill_plan {
   int64_t workspace_bytes; /* workspace the split plan needs (0: nothing is split) */
 } astr_prefill_plan;
 
+/* Bytes at the start of a prefill workspace that hold its int32 arrival
+ * counters (one per split query tile).  A fixed region, so that calls with
+ * different plans can share one workspace. */
+#define ASTR_WORKSPACE_COUNTER_BYTES 32768
+
 /* Host-only prefill plan (validates a first; no HIP call unless num_cus <= 0,
  * which asks the current device's CU count).  Returns astr_status. */
 int astr_plan_prefill(const astr_paged_args* a, int32_t num_cus, astr_prefill_plan* out);
@@ -248,12 +253,13 @@ int astr_plan_prefill(const astr_paged_args* a, int32_t num_cus, astr_prefill_pl
  * ([attention.py @c9ceca1], the commit that batches the torch path with a
  * causal offset per request in flat qo_indptr order).
  * workspace: NULL (every query tile runs whole in one work group) or at least
- * astr_plan_prefill's workspace_bytes, 16-byte aligned, whose contents must be
- * ZERO before its first use: it holds the split tiles' partials and arrival
- * counters, and every call leaves the counters at zero again (so one zeroed
- * workspace serves any number of calls; calls that overlap need distinct
- * workspaces).  A non-NULL workspace smaller than the plan needs is
- * ASTR_ERR_WORKSPACE.  Returns astr_status. */
+ * astr_plan_prefill's workspace_bytes, 16-byte aligned.  Its counter region
+ * (the first ASTR_WORKSPACE_COUNTER_BYTES) must be ZERO before its first use;
+ * the split tiles' partials follow it, and every call leaves the counters at
+ * zero again, so one zeroed workspace serves any number of calls of any plan
+ * (calls that overlap need distinct workspaces).  A plan with more split
+ * tiles than the region holds keeps every tile whole.  A non-NULL workspace
+ * smaller than the plan needs is ASTR_ERR_WORKSPACE.  Returns astr_status. */
 int astr_paged_prefill(const astr_paged_args* a, void* workspace, size_t workspace_bytes, void* stream);
 
 /* The K and V rows of a step's new tokens, bf16, [rows, Hkv, D]: element

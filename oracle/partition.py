@@ -184,10 +184,13 @@ def decode_via_splits(q_bits, k_pool_bits, v_pool_bits, req_to_token, req_to_tok
 # key tiles over all (tile, kv head) / S)), a tile is cut into
 # ns = min(16, ceil(nt / T)) chunks, chunk s covering key tiles
 # [floor(nt*s/ns), floor(nt*(s+1)/ns)) -- but only when the whole tiles,
-# times Hkv, number fewer than S / 2 (otherwise every ns is 1).  The plan
+# times Hkv, number fewer than S / 2 (otherwise every ns is 1), and only
+# while the chunks of split tiles, times Hkv, fit the workspace's counter
+# region (8192 counters at its start, before the partials).  The plan
 # applies to the automatic grid of at most 96 requests.
 
-PREFILL = {"rows": 128, "key_tile": 64, "min_chunk_tiles": 8, "max_chunks": 16, "max_reqs": 96}
+PREFILL = {"rows": 128, "key_tile": 64, "min_chunk_tiles": 8, "max_chunks": 16, "max_reqs": 96,
+           "counter_bytes": 32768}
 
 
 def prefill_tiles(qo_indptr, kv_indptr, group, non_causal=False):
@@ -223,8 +226,11 @@ def prefill_plan(qo_indptr, kv_indptr, num_qo_heads, num_kv_heads, head_dim, num
     split_chunks = sum(n for n in ns.values() if n > 1) * num_kv_heads
     split_tiles = sum(1 for n in ns.values() if n > 1) * num_kv_heads
     part_one = 4 * 2 * (head_dim // 16) * 64 * 16 + 4 * 2 * 64 * 8
+    if split_chunks > PREFILL["counter_bytes"] // 4:
+        return prefill_plan(qo_indptr, kv_indptr, num_qo_heads, num_kv_heads, head_dim, num_cus, non_causal,
+                            split=False)
     partial_bytes = split_chunks * part_one
-    ws = (_ceil_div(partial_bytes, 256) * 256 + split_chunks * 4) if split_chunks else 0
+    ws = PREFILL["counter_bytes"] + partial_bytes if split_chunks else 0
     return {"num_items": items, "split_tiles": split_tiles, "chunk_tiles": T, "max_chunks": max_chunks,
             "partial_bytes": partial_bytes, "workspace_bytes": ws}, ns
 

@@ -24,6 +24,7 @@ ASTR_ERR_WORKSPACE = 3
 ASTR_ERR_HIP = 4
 DEFAULT_MAX_SPLITS = 256
 NOALLOC_SCRATCH_BYTES = 32 << 20   # ASTR_NOALLOC_SCRATCH_BYTES
+WORKSPACE_COUNTER_BYTES = 32768     # ASTR_WORKSPACE_COUNTER_BYTES: zeroed counter region opening a prefill workspace
 
 EXPORTED = ("astr_workspace_size", "astr_plan_decode", "astr_paged_decode", "astr_paged_decode_noalloc",
             "astr_plan_prefill", "astr_paged_prefill",
@@ -231,7 +232,7 @@ def astr_paged_decode(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host
                       mask=None, page_size=1):
     """Paged GQA decode: q [B, Hq, D] bf16 -> o [B, Hq, D] bf16 (+ lse [B, Hq] fp32).
 
-    timing_events: optional 4 HipEvent (hip_events.py): start/end stamps of the
+    timing_events: optional 4 HipEvent or None (hip_events.py): start/end stamps of the
     split kernel, then of the combine kernel (None entries are skipped)."""
     if timing_events is not None and len(timing_events) != 4:
         raise ValueError("decode timing_events takes 4 events (split start/end, combine start/end)")

@@ -61,6 +61,8 @@ int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
+static_assert(astr::kCounterBytes == ASTR_WORKSPACE_COUNTER_BYTES, "counter region size");
+
 int64_t partial_bytes(int64_t batch, int64_t hq, int64_t d, int64_t splits) {
   const int64_t P = splits + batch - 1;
   return align256(hq * P * d * 4) + hq * P * 2 * 4;
@@ -371,12 +373,17 @@ void plan_prefill_impl(const astr_paged_args* a, int32_t num_cus, bool split, as
   w->req[B] = astr::PrefillWorkReq{0, (int32_t)first, (int32_t)split_first, 0, 0, 0, 0};
   w->num_reqs = B;
   const int64_t split_slots = w->slices * split_first;
+  if (split_slots > astr::kCounterWords) {
+    // More split tiles than the workspace's counter region holds: keep every tile whole.
+    plan_prefill_impl(a, num_cus, false, w, out);
+    return;
+  }
   out->num_items = (int32_t)(w->slices * first);
   out->split_tiles = (int32_t)(split_tiles * a->num_kv_heads);
   out->chunk_tiles = w->chunk_tiles;
   out->max_chunks = w->max_chunks;
   out->partial_bytes = split_slots * astr::prefill_partial_bytes(a->head_dim);
-  out->workspace_bytes = split_slots > 0 ? align256(out->partial_bytes) + split_slots * 4 : 0;
+  out->workspace_bytes = split_slots > 0 ? astr::kCounterBytes + out->partial_bytes : 0;
 }
 
 // Whether a prefill call can take the work-list path (automatic plan, batch
@@ -707,8 +714,8 @@ int astr_paged_prefill(const astr_paged_args* a, void* workspace, size_t workspa
         // Beyond one 32-bit buffer range: keep every tile whole.
         plan_prefill_impl(a, num_cus, false, &p.work, &plan);
       } else {
-        p.part = static_cast<char*>(workspace);
-        p.cnt = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + align256(plan.partial_bytes));
+        p.cnt = static_cast<int32_t*>(workspace);
+        p.part = static_cast<char*>(workspace) + astr::kCounterBytes;
         p.part_bytes = (uint32_t)plan.partial_bytes;
       }
     }

@@ -7,6 +7,14 @@
 
 namespace astr {
 
+// Arrival counters at the start of a prefill workspace, one per split query
+// tile.  They must be zero before the first call on a workspace and every
+// call leaves them zero; a fixed region, so that calls with different plans
+// can share one workspace (a counter never lands on an earlier call's
+// partials).  The chunk partials follow it.
+constexpr int64_t kCounterWords = 8192;
+constexpr int64_t kCounterBytes = kCounterWords * 4;
+
 struct DecodeLaunch {
   int32_t batch, num_qo_heads, num_kv_heads, head_dim, group;
   float sm_scale;

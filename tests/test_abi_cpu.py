@@ -27,6 +27,10 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, name), name
     version = int(re.search(r"#define ASTR_ABI_VERSION (\d+)", header).group(1))
     assert lib.astr_abi_version() == version
+    # Byte constants the binding mirrors.
+    assert int(re.search(r"#define ASTR_WORKSPACE_COUNTER_BYTES (\d+)", header).group(1)) == _lib.WORKSPACE_COUNTER_BYTES
+    m = re.search(r"#define ASTR_NOALLOC_SCRATCH_BYTES \((\d+)ull << (\d+)\)", header)
+    assert int(m.group(1)) << int(m.group(2)) == _lib.NOALLOC_SCRATCH_BYTES
 
 
 def test_workspace_size_formula(lib):

@@ -47,9 +47,9 @@ def _check_split_and_whole(inp, what, min_split=1, **kw):
     announce(f"prefill split {what}: items={plan.num_items} split_tiles={plan.split_tiles} "
              f"chunk_tiles={plan.chunk_tiles}")
     o_s, lse_s = _run(dev, ws, **kw)
-    c0 = ((plan.partial_bytes + 255) // 256) * 256 // 4          # counters follow the partials
-    n_cnt = (plan.workspace_bytes // 4) - c0
-    assert n_cnt > 0 and bool((ws[c0:c0 + n_cnt] == 0).all()), f"{what}: arrival counters not reset"
+    n_cnt = _lib.WORKSPACE_COUNTER_BYTES // 4                    # the counter region opens the workspace
+    assert plan.workspace_bytes == _lib.WORKSPACE_COUNTER_BYTES + plan.partial_bytes
+    assert bool((ws[:n_cnt] == 0).all()), f"{what}: arrival counters not reset"
     announce(f"prefill whole {what}")
     o_w, lse_w = _run(dev, None, **kw)
     ref_o = ref_lse = None
@@ -94,21 +94,28 @@ def test_prefill_split_long_prefixes(Hq, Hkv, D):
 
 
 def test_prefill_split_reuses_one_workspace():
-    """One zeroed workspace serves consecutive calls (the counters are left at zero): the same
-    inputs give the same bits every time, and other inputs in between do not disturb them."""
+    """One zeroed workspace serves consecutive calls of different plans (the counters, at the
+    start of the workspace, are left at zero): the same inputs give the same bits every time,
+    other inputs in between do not disturb them, and a smaller plan after a larger one (whose
+    partials cover more of the workspace) is still right."""
     a = build_paged_inputs(np.array([3000, 1800, 400]), 32, 8, 128, 1 << 14, seed=91, q_lens=np.array([64, 500, 33]))
     b = build_paged_inputs(np.array([2500, 90]), 32, 8, 128, 1 << 14, seed=92, q_lens=np.array([100, 90]))
     da, db = tensors.to_device(a, DEV), tensors.to_device(b, DEV)
     wa, wb = tensors.prefill_workspace(da), tensors.prefill_workspace(db)
     ws = torch.zeros(max(wa.numel(), wb.numel()), dtype=torch.int32, device=DEV)
     announce("prefill split: one workspace, five calls")
+    pa, pb = _plan(da), _plan(db)
+    assert pa.split_tiles > 0 and pb.split_tiles > 0 and pa.partial_bytes > pb.partial_bytes
+    ref_b, _ = oracle_of(b)
     first, _ = _run(da, ws)
     for rep in range(2):
-        _run(db, ws)
+        ob, _ = _run(db, ws)
+        assert_close(ob, ref_b, f"reused workspace, smaller plan, call {rep} O", ulp_check=False)
         again, _ = _run(da, ws)
         assert torch.equal(first.view(torch.int16), again.view(torch.int16)), f"call {rep}"
     ref_o, _ = oracle_of(a)
     assert_close(first, ref_o, "reused workspace O", ulp_check=False)
+    assert bool((ws[: _lib.WORKSPACE_COUNTER_BYTES // 4] == 0).all()), "arrival counters not reset"
 
 
 def test_prefill_split_with_masks_and_noncausal():
