@@ -370,23 +370,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefil
       // reads back next to their first use, where each pair would wait out a
       // full LDS latency.
       f32x4 st[2][4];
-      bf16x8 ka[2][NS];
+      // At head_dim 256 one block's K operands are 32 registers and the
+      // wavefront's other state fills the register file, so the next block's
+      // are not read ahead there (reading them ahead spilled to scratch).
+      constexpr int KBUF = D == 256 ? 1 : 2;
+      bf16x8 ka[KBUF][NS];
   #pragma unroll
       for (int ks = 0; ks < NS; ++ks) ka[0][ks] = *reinterpret_cast<const bf16x8*>(&kt[l16 * D + 8 * ((4 * ks + kb) ^ swk)]);
   #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
-        if (tb < 3) {
+        if (KBUF == 1 && tb > 0) {
   #pragma unroll
           for (int ks = 0; ks < NS; ++ks)
-            ka[(tb + 1) & 1][ks] = *reinterpret_cast<const bf16x8*>(&kt[(16 * (tb + 1) + l16) * D + 8 * ((4 * ks + kb) ^ swk)]);
+            ka[0][ks] = *reinterpret_cast<const bf16x8*>(&kt[(16 * tb + l16) * D + 8 * ((4 * ks + kb) ^ swk)]);
         }
-        __builtin_amdgcn_sched_barrier(0);
+        if (KBUF == 2 && tb < 3) {
+  #pragma unroll
+          for (int ks = 0; ks < NS; ++ks)
+            ka[(tb + 1) % KBUF][ks] = *reinterpret_cast<const bf16x8*>(&kt[(16 * (tb + 1) + l16) * D + 8 * ((4 * ks + kb) ^ swk)]);
+        }
+        if constexpr (KBUF == 2) __builtin_amdgcn_sched_barrier(0);
         st[0][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
         st[1][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
   #pragma unroll
         for (int ks = 0; ks < NS; ++ks) {
-          st[0][tb] = mfma32k(ka[tb & 1][ks], qop[0][ks], st[0][tb]);
-          st[1][tb] = mfma32k(ka[tb & 1][ks], qop[1][ks], st[1][tb]);
+          st[0][tb] = mfma32k(ka[tb % KBUF][ks], qop[0][ks], st[0][tb]);
+          st[1][tb] = mfma32k(ka[tb % KBUF][ks], qop[1][ks], st[1][tb]);
         }
       }
 
