@@ -98,7 +98,9 @@ def build_probes(verbose: bool = False):
             continue
         src = os.path.join(PROBES, f)
         exe = os.path.join(PROBES, f[:-4])
-        cmd = [hipcc(), "-O3", "-std=c++17"] + HIP_FLAGS + [src, "-o", exe]
+        # Probes may call the library (include/astr_attn.h, linked from the package directory).
+        cmd = [hipcc(), "-O3", "-std=c++17"] + HIP_FLAGS + ["-I", os.path.join(ROOT, "include"), src, "-o", exe,
+                                                            "-L", PKG, "-lastr_attn", "-Wl,-rpath,$ORIGIN/.."]
         res = subprocess.run(cmd, capture_output=True, text=True)
         if res.returncode != 0:
             raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
