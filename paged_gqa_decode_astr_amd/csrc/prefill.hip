@@ -8,11 +8,13 @@
 // prefill kernel tiles over queries and uses matrix instructions for QK^T and
 // PV; query head h reads kv head h / G.
 //
-// Work group = (query tile, kv head g, request b), 4 wavefronts, on a 1-D
-// grid laid out for the per-XCD L2s (see the work-item mapping below).  The
-// G query heads that share kv head g are stacked with the positions into 128
-// rows (row R = position * G + head), so each K/V tile staged in LDS serves
-// all of them; wavefront w owns rows 32 w .. 32 w + 31 as two 16-row blocks.
+// Work group = (query tile, kv head g, request b) on a 1-D grid laid out
+// for the per-XCD L2s (see the work-item mapping below).  The G query heads
+// that share kv head g are stacked with the positions into 128 rows (row
+// R = position * G + head), so each K/V tile staged in LDS serves all of
+// them.  Up to head_dim 128 a work group is 4 wavefronts and wavefront w owns
+// rows 32 w .. 32 w + 31 as two 16-row blocks; at head_dim 256 it is 8
+// wavefronts of one 16-row block each (see prefill_row_blocks).
 // Per 64-key tile:
 //   * K and V rows are gathered through req_to_token straight into LDS
 //     (global_load_lds, 16 bytes per lane) one tile ahead, slot ids one more
@@ -65,8 +67,17 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 
-constexpr int kThreads = 256;
 constexpr int kRows = 128;       // (position, head) rows per work group
+// 16-row blocks per wavefront: two up to head_dim 128 (each K and V operand
+// read from LDS feeds two MFMAs), one at 256, where two blocks' accumulators
+// and operands overflowed the registers of the one wavefront per SIMD that
+// fit; with one block the work group has 8 wavefronts, two per SIMD.
+template <int D>
+constexpr int prefill_row_blocks() { return D == 256 ? 1 : 2; }
+template <int D>
+constexpr int prefill_waves() { return kRows / (16 * prefill_row_blocks<D>()); }   // per work group
+template <int D>
+constexpr int prefill_threads() { return prefill_waves<D>() * kWave; }
 constexpr int KT = 64;           // keys per tile
 constexpr float kTau = 8.0f;     // log2 headroom before the accumulators are rescaled
 constexpr int kXcds = 8;         // accelerator dies a launch is dealt across
@@ -90,11 +101,11 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 // (the loads see what other work groups released at agent scope, on any XCD).
 constexpr int kScopeAgent = 16;
 
-// Waves per SIMD: two up to head_dim 128; at 256 the accumulators and
-// operands of a wavefront's 32 rows need the whole register file (one wave,
-// accumulators in AGPRs), and the K/V stages take 128 KB of LDS.
+// Waves per SIMD the kernel is built for: two (two 4-wavefront work groups
+// per CU up to head_dim 128; one 8-wavefront work group at 256, whose K/V
+// stages take 128 KB of LDS).
 template <int D>
-constexpr int prefill_waves_per_simd() { return D == 256 ? 1 : 2; }
+constexpr int prefill_waves_per_simd() { return 2; }
 
 // The (query tile, chunk) a work group runs and its key tiles [it_lo, it_hi).
 struct PrefillItem {
@@ -115,11 +126,13 @@ __device__ __forceinline__ int tile_chunks(int nt, const PrefillWork& w) {
 }
 
 template <int D, int G, bool OFF32, bool MASK, bool WORK>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefill_waves_per_simd<D>()))) void prefill_kernel(const PrefillLaunch p) {
+__global__ __launch_bounds__(prefill_threads<D>()) __attribute__((amdgpu_waves_per_eu(prefill_waves_per_simd<D>()))) void prefill_kernel(const PrefillLaunch p) {
   using S = PShape<D>;
   constexpr int BQ = kRows / G;   // query positions per work group
   constexpr int NS = S::kSteps;
   constexpr int NB = S::kDBlocks;
+  constexpr int kRB = prefill_row_blocks<D>();
+  constexpr int kWavesWg = prefill_waves<D>();
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   // Two stages, each its own array, so that the compiler can tell the LDS
@@ -232,7 +245,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefil
   // global addresses.
   constexpr int CPR = D / 8;
   constexpr int RPI = kWave / CPR;
-  constexpr int NI = KT / RPI / (kThreads / kWave);
+  constexpr int NT = KT / RPI;                                   // load instructions per K (or V) tile
+  constexpr int NI = NT >= kWavesWg ? NT / kWavesWg : 1;          // per wavefront
+  static_assert(NT % NI == 0 && NT / NI <= kWavesWg, "tile rows split evenly over the loading wavefronts");
+  // When a tile is fewer load instructions than there are wavefronts, only
+  // the first NT / NI wavefronts gather (uniform per wavefront); otherwise
+  // the test is compiled out (a branch there cost the head_dim 128 kernel 7%).
+  [[maybe_unused]] const bool loader = NI * wv < NT;
+  constexpr bool kSomeIdle = NT < kWavesWg;
   // The swizzle stays below the row's chunk count: at D = 32 a row has only
   // 4 chunks, and an XOR value of 4 or more would address the next row.
   auto swz = [](int r) { return D >= 128 ? 2 * (r & 7) : (D == 64 ? 2 * ((r >> 1) & 3) : (r >> 1) & 3); };
@@ -252,6 +272,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefil
   }
   int id_next[NI];
   auto load_ids = [&](int t0) {
+    if constexpr (kSomeIdle) {
+      if (!loader) return;
+    }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int t = min(t0 + grow0 + RPI * i, kv_end - 1);
@@ -262,6 +285,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefil
   };
   // Tile starting at key t0: slot of row i's key from its table entry.
   auto gather = [&](uint16_t* kdst, uint16_t* vdst, int t0) {
+    if constexpr (kSomeIdle) {
+      if (!loader) return;
+    }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int row0 = RPI * (NI * wv + i);
@@ -291,11 +317,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefil
   load_ids((it_lo + 1) * KT);
 
   // B operand of S^T = K Q^T: lane (r + 16 kb) holds Q[row r][32 ks + 8 kb .. +7] of each row block.
-  bf16x8 qop[2][NS];
-  int lim[2];
+  bf16x8 qop[kRB][NS];
+  int lim[kRB];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int R = 32 * wv + 16 * rb + l16;
+  for (int rb = 0; rb < kRB; ++rb) {
+    const int R = 16 * (kRB * wv + rb) + l16;
     const int posl = R / G;
     const int head = g * G + R % G;
     lim[rb] = p.non_causal ? L - 1 : cofs + p0 + posl;  // last key this row may see
@@ -313,12 +339,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefil
   // one dword per (rb, tb), loaded one tile ahead through a buffer resource
   // over the request's mask block, whose range check returns 0 (hidden) for
   // anything past it.  A 2-D mask has row stride 0.
-  [[maybe_unused]] uint32_t mcur[2][4], mnext[2][4];
-  [[maybe_unused]] uint32_t mrow[2];
+  [[maybe_unused]] uint32_t mcur[kRB][4], mnext[kRB][4];
+  [[maybe_unused]] uint32_t mrow[kRB];
   [[maybe_unused]] __amdgpu_buffer_rsrc_t mrs;
-  auto load_mask = [&](int t0, uint32_t (&dst)[2][4]) {
+  auto load_mask = [&](int t0, uint32_t (&dst)[kRB][4]) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
         dst[rb][tb] = __builtin_amdgcn_raw_buffer_load_b32(mrs, mrow[rb] + (uint32_t)(t0 + 16 * tb + 4 * kb), 0, 0);
@@ -327,19 +353,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefil
     mrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.mask + (int64_t)b * p.mask_stride_req), (short)0,
                                             (int)p.mask_stride_req, 0x00020000);
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) mrow[rb] = (uint32_t)((p0 + (32 * wv + 16 * rb + l16) / G) * p.mask_stride_row);
+    for (int rb = 0; rb < kRB; ++rb) mrow[rb] = (uint32_t)((p0 + (16 * (kRB * wv + rb) + l16) / G) * p.mask_stride_row);
     load_mask(it_lo * KT, mcur);
   }
   const float qk_scale = p.sm_scale * kLog2e;
   const int lim_min = p.non_causal ? L - 1 : cofs + p0;   // smallest row limit of the work group
-  f32x4 acc[2][NB];
-  f32x4 lacc[2];     // row sums of the weights (all four entries of a lane equal)
-  float mref[2];
+  f32x4 acc[kRB][NB];
+  f32x4 lacc[kRB];     // row sums of the weights (all four entries of a lane equal)
+  float mref[kRB];
   bf16x8 ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < kRB; ++rb) {
     mref[rb] = -INFINITY;
     lacc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -369,7 +395,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefil
       // MFMAs run; the scheduling fences keep the compiler from pulling the
       // reads back next to their first use, where each pair would wait out a
       // full LDS latency.
-      f32x4 st[2][4];
+      f32x4 st[kRB][4];
       // At head_dim 256 one block's K operands are 32 registers and the
       // wavefront's other state fills the register file, so the next block's
       // are not read ahead there (reading them ahead spilled to scratch).
@@ -390,20 +416,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefil
             ka[(tb + 1) % KBUF][ks] = *reinterpret_cast<const bf16x8*>(&kt[(16 * (tb + 1) + l16) * D + 8 * ((4 * ks + kb) ^ swk)]);
         }
         if constexpr (KBUF == 2) __builtin_amdgcn_sched_barrier(0);
-        st[0][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        st[1][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
   #pragma unroll
-        for (int ks = 0; ks < NS; ++ks) {
-          st[0][tb] = mfma32k(ka[tb % KBUF][ks], qop[0][ks], st[0][tb]);
-          st[1][tb] = mfma32k(ka[tb % KBUF][ks], qop[1][ks], st[1][tb]);
-        }
+        for (int rb = 0; rb < kRB; ++rb) st[rb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+        for (int ks = 0; ks < NS; ++ks)
+  #pragma unroll
+          for (int rb = 0; rb < kRB; ++rb) st[rb][tb] = mfma32k(ka[tb % KBUF][ks], qop[rb][ks], st[rb][tb]);
       }
 
       // Causal mask (only tiles that reach past the first row's limit need
       // it), and the boolean mask (every tile of a MASK work group).
       if constexpr (decltype(masked)::value) {
   #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
+        for (int rb = 0; rb < kRB; ++rb) {
           const int thr = lim[rb] - t0 - 4 * kb;   // key 16 tb + q of this lane is visible iff <= thr
   #pragma unroll
           for (int tb = 0; tb < 4; ++tb)
@@ -415,9 +440,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefil
             }
         }
       }
-      bf16x8 pop[2][2];
+      bf16x8 pop[kRB][2];
   #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
+      for (int rb = 0; rb < kRB; ++rb) {
         // Exponents against the current reference: x = s - mref (base 2).  The
         // common case needs only this lane's maximum: if no x exceeds kTau the
         // reference stands and no cross-lane step is taken.  A NaN maximum
@@ -485,16 +510,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefil
         if (db + 1 < NB) vread(db + 1, va[(db + 1) & 1]);
         __builtin_amdgcn_sched_barrier(0);
   #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          acc[0][db] = mfma32k(va[db & 1][k2], pop[0][k2], acc[0][db]);
-          acc[1][db] = mfma32k(va[db & 1][k2], pop[1][k2], acc[1][db]);
-        }
+        for (int k2 = 0; k2 < 2; ++k2)
+  #pragma unroll
+          for (int rb = 0; rb < kRB; ++rb) acc[rb][db] = mfma32k(va[db & 1][k2], pop[rb][k2], acc[rb][db]);
       }
 
       stage_ready();   // the next stage is loaded; this one may be overwritten
       if constexpr (MASK) {
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+        for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
           for (int tb = 0; tb < 4; ++tb) mcur[rb][tb] = mnext[rb][tb];
       }
@@ -517,7 +541,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefil
   run_tiles(std::true_type{}, it_plain, it_hi);
 
   // acc[rb][db][q] = O^T[d = 16 db + 4 kb + q][row 16 rb + l16], relative to mref.
-  float ltot[2] = {lacc[0][0], lacc[1][0]};
+  float ltot[kRB];
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) ltot[rb] = lacc[rb][0];
   if (WORK && it.ns > 1) {
     // Split tile: leave this chunk's state in its slot (lane-major, so every
     // access is one contiguous 1 KB per instruction) with agent-coherent
@@ -526,18 +552,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefil
     // would also write back the whole L2 of the XCD, which measured 2x slower
     // for the kernel; the stores that must be seen are all coherent already.)
     const uint32_t slot_off = (uint32_t)it.slot * (uint32_t)prefill_partial_bytes(D);
-    const uint32_t ml_off = 4u * 2u * NB * kWave * 16u;
+    const uint32_t ml_off = (uint32_t)(kRows / 16) * NB * kWave * 16u;   // after the (wavefront, row block) accumulators
     __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(p.part, (short)0, (int)p.part_bytes, 0x00020000);
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < kRB; ++rb) {
 #pragma unroll
       for (int db = 0; db < NB; ++db)
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[rb][db]), prs,
-                                               slot_off + 16u * (((wv * 2 + rb) * NB + db) * kWave + lane), 0,
+                                               slot_off + 16u * (((wv * kRB + rb) * NB + db) * kWave + lane), 0,
                                                kScopeAgent);
       const float2 ml = make_float2(mref[rb], ltot[rb]);
       __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ml), prs,
-                                            slot_off + ml_off + 8u * ((wv * 2 + rb) * kWave + lane), 0, kScopeAgent);
+                                            slot_off + ml_off + 8u * ((wv * kRB + rb) * kWave + lane), 0, kScopeAgent);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wavefront's slot stores have completed
     // The arrival count is broadcast through the first word of a K stage,
@@ -555,7 +581,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefil
     // last; then reset the counter for the next call.
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < kRB; ++rb) {
       mref[rb] = -INFINITY;
       ltot[rb] = 0.f;
 #pragma unroll
@@ -563,19 +589,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefil
     }
     for (int s2 = 0; s2 < it.ns; ++s2) {
       const uint32_t o2 = (uint32_t)(it.tile_slot + s2 * p.work.slices) * (uint32_t)prefill_partial_bytes(D);
-      float2 ml2[2];
-      f32x4 a2[2][NB];
+      float2 ml2[kRB];
+      f32x4 a2[kRB][NB];
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
+      for (int rb = 0; rb < kRB; ++rb) {
         ml2[rb] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(
-                                                 prs, o2 + ml_off + 8u * ((wv * 2 + rb) * kWave + lane), 0, kScopeAgent));
+                                                 prs, o2 + ml_off + 8u * ((wv * kRB + rb) * kWave + lane), 0, kScopeAgent));
 #pragma unroll
         for (int db = 0; db < NB; ++db)
           a2[rb][db] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                     prs, o2 + 16u * (((wv * 2 + rb) * NB + db) * kWave + lane), 0, kScopeAgent));
+                                                     prs, o2 + 16u * (((wv * kRB + rb) * NB + db) * kWave + lane), 0, kScopeAgent));
       }
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
+      for (int rb = 0; rb < kRB; ++rb) {
         // A chunk with no visible key for the row has max -inf and sum 0.
         const float mnew = fmaxf(mref[rb], ml2[rb].x);
         const float c1 = mref[rb] == -INFINITY ? 0.f : exp2f(mref[rb] - mnew);
@@ -589,8 +615,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefil
     if (tid == 0) __hip_atomic_store(p.cnt + it.tile_slot, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int R = 32 * wv + 16 * rb + l16;
+  for (int rb = 0; rb < kRB; ++rb) {
+    const int R = 16 * (kRB * wv + rb) + l16;
     const int posl = R / G;
     if (posl >= npos) continue;
     const int row = q0 + p0 + posl;
@@ -613,11 +639,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefil
 template <int D, int G, bool WORK>
 hipError_t launch_w(const PrefillLaunch& p, dim3 grid, hipStream_t s, const Timing& t) {
   if (p.mask != nullptr) {
-    if (p.off32) return launch_kernel(prefill_kernel<D, G, true, true, WORK>, grid, dim3(kThreads), s, t, p);
-    return launch_kernel(prefill_kernel<D, G, false, true, WORK>, grid, dim3(kThreads), s, t, p);
+    if (p.off32) return launch_kernel(prefill_kernel<D, G, true, true, WORK>, grid, dim3(prefill_threads<D>()), s, t, p);
+    return launch_kernel(prefill_kernel<D, G, false, true, WORK>, grid, dim3(prefill_threads<D>()), s, t, p);
   }
-  if (p.off32) return launch_kernel(prefill_kernel<D, G, true, false, WORK>, grid, dim3(kThreads), s, t, p);
-  return launch_kernel(prefill_kernel<D, G, false, false, WORK>, grid, dim3(kThreads), s, t, p);
+  if (p.off32) return launch_kernel(prefill_kernel<D, G, true, false, WORK>, grid, dim3(prefill_threads<D>()), s, t, p);
+  return launch_kernel(prefill_kernel<D, G, false, false, WORK>, grid, dim3(prefill_threads<D>()), s, t, p);
 }
 
 template <int D, int G>
