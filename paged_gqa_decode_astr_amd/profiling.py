@@ -416,9 +416,11 @@ def main(argv=None):
         if args.config == "decode_b32":
             args.config = "prefill_b8"
         return _prefill_pmc(args)
-    # Default: the decode timing legs of bench.py only (its graph and append legs launch the same
-    # kernel at other shapes, which would enter the kernel's average).
-    return _trace(args, bench_args or ["--cpu-seconds", "0", "--no-graph", "--no-append", "--no-warm"])
+    # Default: the headline decode leg of bench.py (and its masked variant, a kernel of its own) only:
+    # its other legs -- the other decode workloads, graph and append -- launch the same kernel at
+    # other shapes, which would enter the kernel's average.
+    return _trace(args, bench_args or ["--cpu-seconds", "0", "--no-graph", "--no-append", "--no-warm",
+                                       "--no-configs", "--no-prefill"])
 
 
 if __name__ == "__main__":
