@@ -180,14 +180,14 @@ def decode_via_splits(q_bits, k_pool_bits, v_pool_bits, req_to_token, req_to_tok
 #
 # This project's split rule (the pages only say that long key ranges are
 # split into partials merged by a combine step, for decode): with S slots
-# (two work groups per CU, one at head_dim 256) and T = max(8, ceil(total
-# key tiles over all (tile, kv head) / S)), a tile is cut into
-# ns = min(16, ceil(nt / T)) chunks, chunk s covering key tiles
-# [floor(nt*s/ns), floor(nt*(s+1)/ns)) -- but only when the whole tiles,
-# times Hkv, number fewer than S / 2 (otherwise every ns is 1), and only
-# while the chunks of split tiles, times Hkv, fit the workspace's counter
-# region (8192 counters at its start, before the partials).  The plan
-# applies to the automatic grid of at most 96 requests.
+# (two work groups per CU, one at head_dim 256), a tile of nt key tiles is cut
+# into ns = min(16, ceil(nt / T)) chunks, chunk s covering key tiles
+# [floor(nt*s/ns), floor(nt*(s+1)/ns)), where T is the smallest chunk length
+# of at least 8 key tiles at which all chunks, times Hkv, still fit in S --
+# and nothing is split when the whole tiles, times Hkv, already number more
+# than S, or when the chunks of split tiles, times Hkv, would not fit the
+# workspace's counter region (8192 counters at its start, before the
+# partials).  The plan applies to the automatic grid of at most 96 requests.
 
 PREFILL = {"rows": 128, "key_tile": 64, "min_chunk_tiles": 8, "max_chunks": 16, "max_reqs": 96,
            "counter_bytes": 32768}
@@ -217,9 +217,19 @@ def prefill_plan(qo_indptr, kv_indptr, num_qo_heads, num_kv_heads, head_dim, num
         return None, {}
     tiles = prefill_tiles(qo_indptr, kv_indptr, group, non_causal)
     slots = (1 if head_dim == 256 else 2) * num_cus
-    total = sum(nt for _, _, nt in tiles) * num_kv_heads
-    T = max(PREFILL["min_chunk_tiles"], _ceil_div(total, slots))
-    splitting = split and 2 * len(tiles) * num_kv_heads < slots
+
+    def items_at(T):
+        return sum(min(PREFILL["max_chunks"], _ceil_div(nt, T)) for _, _, nt in tiles) * num_kv_heads
+
+    T = max(PREFILL["min_chunk_tiles"], max(nt for _, _, nt in tiles))
+    splitting = split and items_at(T) <= slots
+    if splitting:
+        # The smallest T >= min_chunk_tiles with items_at(T) <= slots, by trying each in turn
+        # (items_at only falls as T grows).
+        for t in range(PREFILL["min_chunk_tiles"], T + 1):
+            if items_at(t) <= slots:
+                T = t
+                break
     max_chunks = PREFILL["max_chunks"] if splitting else 1
     ns = {(b, qt): min(max_chunks, _ceil_div(nt, T)) for b, qt, nt in tiles}
     items = sum(ns.values()) * num_kv_heads

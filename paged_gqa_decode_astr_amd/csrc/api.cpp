@@ -275,11 +275,7 @@ constexpr int64_t kPrefillRows = 128;
 #ifndef ASTR_PREFILL_MIN_CHUNK_TILES
 #define ASTR_PREFILL_MIN_CHUNK_TILES 8
 #endif
-#ifndef ASTR_PREFILL_CHUNK_PCT
-#define ASTR_PREFILL_CHUNK_PCT 100
-#endif
 constexpr int64_t kMinChunkTiles = ASTR_PREFILL_MIN_CHUNK_TILES;
-constexpr int64_t kChunkPct = ASTR_PREFILL_CHUNK_PCT;   // chunk length as a percentage of the balanced share
 constexpr int32_t kMaxChunks = astr::kPrefillMaxChunks;
 int64_t prefill_wg_per_cu(int32_t head_dim) { return head_dim == 256 ? 1 : 2; }
 
@@ -303,25 +299,44 @@ void plan_prefill_impl(const astr_paged_args* a, int32_t num_cus, bool split, as
   const int32_t* qo = a->qo_indptr_host;
   const int32_t* kv = a->kv_indptr_host;
   std::vector<int64_t> work(B), biggest(B);
-  int64_t total = 0;
   for (int32_t b = 0; b < B; ++b) {
     const int64_t qb = qo[b + 1] - qo[b], L = kv[b + 1] - kv[b];
     int64_t wsum = 0;
     for (int64_t qt = 0; qt * BQ < qb; ++qt) wsum += prefill_tile_keys(qt, BQ, qb, L, nc);
     work[b] = wsum;
-    total += wsum * a->num_kv_heads;
   }
   const int64_t slots = prefill_wg_per_cu(a->head_dim) * (int64_t)(num_cus > 0 ? num_cus : 1);
-  const int64_t T = std::max<int64_t>(kMinChunkTiles, ceil_div(ceil_div(total, slots) * kChunkPct, 100));
+  // The chunk length T: the shortest (at least kMinChunkTiles key tiles) at
+  // which all items still fit in one round of work-group slots, so that every
+  // chunk starts at once and the longest item is as short as one round
+  // allows (measured: a plan that needs a second round, or one that leaves
+  // slots idle with longer chunks, is slower).  When the whole tiles alone
+  // fill the slots, nothing is split.
+  std::vector<int64_t> nts;
+  int64_t max_nt = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t qb = qo[b + 1] - qo[b], L = kv[b + 1] - kv[b];
+    for (int64_t qt = 0; qt * BQ < qb; ++qt) {
+      nts.push_back(prefill_tile_keys(qt, BQ, qb, L, nc));
+      max_nt = std::max(max_nt, nts.back());
+    }
+  }
+  auto items_at = [&](int64_t T) {
+    int64_t n = 0;
+    for (const int64_t nt : nts) n += std::min<int64_t>(kMaxChunks, ceil_div(nt, T));
+    return n * a->num_kv_heads;
+  };
+  const bool splitting = split && items_at(std::max(kMinChunkTiles, max_nt)) <= slots;
+  int64_t T = std::max(kMinChunkTiles, max_nt);
+  if (splitting) {
+    int64_t lo = kMinChunkTiles;
+    while (lo < T) {
+      const int64_t mid = (lo + T) / 2;
+      if (items_at(mid) <= slots) T = mid; else lo = mid + 1;
+    }
+  }
   w->chunk_tiles = (int32_t)std::min<int64_t>(T, INT32_MAX);
-  // Splitting pays only while whole tiles leave most work-group slots idle:
-  // a CU that holds two work groups already processes key tiles at its full
-  // rate (measured: 2.25 us per 64-key tile per work group at two per CU, about
-  // the rate of one work group alone), so with more whole tiles than half the
-  // slots a split only adds partial traffic and merges.
-  int64_t whole_items = 0;
-  for (int32_t b = 0; b < B; ++b) whole_items += ceil_div((int64_t)qo[b + 1] - qo[b], BQ) * a->num_kv_heads;
-  w->max_chunks = split && 2 * whole_items < slots ? kMaxChunks : 1;
+  w->max_chunks = splitting ? kMaxChunks : 1;
   w->slices = a->num_kv_heads % 8 == 0 ? 8 : 1;
   const int64_t hs = a->num_kv_heads / w->slices;
   // A request's biggest work item: key tiles of its longest chunk or whole

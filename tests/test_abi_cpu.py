@@ -385,11 +385,17 @@ def test_prefill_plan_matches_oracle_random():
 
 
 def test_prefill_plan_examples():
-    # prefill_b8 seed 5000: 448 whole tiles on 256 CUs (>= half of 512 slots): nothing is split.
+    # prefill_b8 seed 5000 on 256 CUs (512 slots): 448 whole tiles, so 64 items to spare.  Request 1
+    # (seq_len 2301, q_len 316) has tiles of 32, 33, 33, 34, 34, ..., 36 key tiles; at T = 32 its
+    # nine tiles above 32 would make 448 + 9 x 8 = 520 items, at T = 33 its seven tiles above 33
+    # make 448 + 7 x 8 = 504, which fits: those seven are halved.
     from paged_gqa_decode_astr_amd.workloads import make_inputs
     inp = make_inputs("prefill_b8", 0)
     a, keep = _prefill_plan_args(inp["qo_indptr"], inp["kv_indptr"])
     p = _lib.astr_plan_prefill(a, 256)
+    assert (p.num_items, p.split_tiles, p.chunk_tiles) == (504, 56, 33)
+    # The same batch on 200 CUs (400 slots): the 448 whole tiles alone exceed them, nothing is split.
+    p = _lib.astr_plan_prefill(a, 200)
     assert (p.num_items, p.split_tiles, p.workspace_bytes) == (448, 0, 0)
     # Two 20000-key requests with 64 new tokens: 16 tiles, each cut 16 ways.
     a, keep = _prefill_plan_args([0, 64, 128], [0, 20000, 40000])

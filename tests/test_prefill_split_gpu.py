@@ -61,12 +61,17 @@ def _check_split_and_whole(inp, what, min_split=1, **kw):
     return o_s, lse_s, o_w, lse_w, ws, ref_o, ref_lse
 
 
-def test_prefill_b8_keeps_tiles_whole():
-    """prefill_b8 has 448 (query tile, kv head) work groups, more than half of the 512 slots of
-    256 CUs: the plan keeps every tile whole (splitting measured no faster there)."""
+def test_prefill_b8_split_plan():
+    """prefill_b8 has 448 (query tile, kv head) work groups against the 512 slots of 256 CUs:
+    the plan halves only its longest tiles, as many as the spare 64 slots allow (7 tiles x 8 kv
+    heads), and the split call matches the whole-tile call and the oracle."""
     inp = make_inputs("prefill_b8", 0)
     plan = _plan(tensors.to_device(inp, DEV))
-    assert plan.num_items == 448 and plan.split_tiles == 0 and plan.workspace_bytes == 0
+    assert plan.num_items == 504 and plan.split_tiles == 56, (plan.num_items, plan.split_tiles)
+    o_s, lse_s, o_w, lse_w, _, ref_o, ref_lse = _check_split_and_whole(inp, "prefill_b8", min_split=56)
+    for o, lse, tag in ((o_s, lse_s, "split"), (o_w, lse_w, "whole")):
+        assert_close(o, ref_o, f"prefill_b8 {tag} O", ulp_check=False)
+        assert_close(lse, ref_lse, f"prefill_b8 {tag} lse", atol=2e-3, rtol=1e-4)
 
 
 @pytest.mark.parametrize("seq,ql", [(20000, 64), (9000, 300), (33000, 1)])
