@@ -223,14 +223,15 @@ int astr_paged_decode_noalloc(const astr_paged_args* a, void* stream);
 
 /* The automatic prefill plan (no fixed grid: max_q_len == 0, batch <= 96).
  * Every query tile (128 / G positions x the G heads of one kv head) is one
- * work group.  When the batch has fewer query tiles than half the device's
- * work-group slots (e.g. a long cached prefix with few new tokens) and a
- * workspace is passed, the key range of a tile with more than about
+ * work group.  With a workspace, the key range of a tile with more than
  * chunk_tiles key tiles (64 keys each) is cut into up to max_chunks (16)
- * chunks run as separate work groups and merged by the last one to finish, so
- * that no work group holds many more keys than the balanced share of the CUs.
- * Other calls (fixed grid, larger batches) keep every tile whole and report
- * num_items = 0. */
+ * chunks run as separate work groups and merged by the last one to finish;
+ * chunk_tiles is the shortest length (at least 8 key tiles) at which all work
+ * groups still fit in one round of the device's work-group slots (two per CU,
+ * one at head_dim 256), so the longest work group is as short as one round
+ * allows.  When the whole tiles alone exceed the slots nothing is split.
+ * Fixed-grid calls (max_q_len set) and batches over 96 requests keep every
+ * tile whole and report num_items = 0. */
 typedef struct astr_prefill_plan {
   int32_t num_items;       /* work groups of the call (0: fixed-grid mapping) */
   int32_t split_tiles;     /* (query tile, kv head) pairs whose key range is split */
