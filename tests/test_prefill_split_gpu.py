@@ -1,8 +1,8 @@
 """GPU parity of prefill with split key ranges (the automatic plan with a workspace).
 
 A query tile whose key range is longer than the plan's chunk length runs as up
-to four work groups, each over a contiguous chunk of the key tiles; the last
-one to finish merges the others' partials.  Every case is compared with the
+to 16 work groups, each over a contiguous chunk of the key tiles; the last one
+to finish merges the others' partials.  Every case is compared with the
 fp64 oracle, and with the same call made without a workspace (every tile whole).
 """
 import numpy as np
