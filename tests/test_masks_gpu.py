@@ -176,6 +176,23 @@ def test_prefill_mask_variants_and_fixed_grid():
         _check(o, lse, ref_o, ref_lse, f"prefill mask Hq={Hq} D={D}", ulp_check=False)
 
 
+@pytest.mark.parametrize("three_d,non_causal", [(False, False), (True, False), (True, True), (None, True)])
+def test_prefill_head_dim_256_masks_and_grids(three_d, non_causal):
+    """head_dim 256 prefill (8 wavefronts of one 16-row block each) with 2-D / 3-D masks and the
+    non-causal switch, on the work-list grid (split plan) and on the fixed grid."""
+    inp = _prefill_case(300 + 3 * (three_d is True) + 2 * (three_d is False) + non_causal, Hq=16, Hkv=4, D=256,
+                        qmax=140, prefix=300)
+    mask = None if three_d is None else _mask(inp, three_d, 0.6, seed=31 + (three_d is True))
+    if three_d:
+        mask[0, 3, :] = 0             # a query row with every key hidden
+    mt = None if mask is None else torch.from_numpy(mask).to(DEV)
+    ref_o, ref_lse = _oracle(inp, mask, non_causal=non_causal)
+    for mq in (0, 200):
+        announce(f"prefill head_dim 256 mask 3d={three_d} non_causal={non_causal} max_q_len={mq}")
+        o, lse = _prefill(inp, mt, non_causal=non_causal, max_q_len=mq)
+        _check(o, lse, ref_o, ref_lse, f"D256 prefill mask 3d={three_d} nc={non_causal} grid={mq}", ulp_check=False)
+
+
 def test_prefill_all_ones_mask_matches_no_mask():
     """An all-ones mask hides nothing: the masked kernel (every tile through the mask code) agrees with
     the oracle run without a mask.  (It is a different kernel from the unmasked one and rounds its bf16
