@@ -334,7 +334,7 @@ __global__ __launch_bounds__(prefill_threads<D>()) __attribute__((amdgpu_waves_p
     }
   }
   // MASK: lane (l16, kb) needs, for each row block rb, the mask bytes of its
-  // row (query p0 + (32 wv + 16 rb + l16) / G of the request) at keys
+  // row (query p0 + (16 (kRB wv + rb) + l16) / G of the request) at keys
   // t0 + 16 tb + 4 kb .. +3:
   // one dword per (rb, tb), loaded one tile ahead through a buffer resource
   // over the request's mask block, whose range check returns 0 (hidden) for
