@@ -24,6 +24,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libastr_attn.so")
+# The same sources built with ASTR_PHASE_STAMPS=1: phase and timeline stamps in
+# the prefill and decode kernels, read by `profiling prefill-phases` and
+# `profiling decode-timeline`.  Never loaded by the tests or the benchmark.
+STAMPS_LIB = os.path.join(PKG, "libastr_attn_stamps.so")
 ARCH = "gfx950"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-Wno-unused-function"]
@@ -42,8 +46,8 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
-def _compile(src: str, extra=()) -> str:
-    obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
+def _compile(src: str, extra=(), objdir: str = OBJDIR) -> str:
+    obj = os.path.join(objdir, os.path.basename(src) + ".o")
     cmd = [hipcc()] + COMMON + list(extra)
     if src.endswith(".hip"):
         cmd += HIP_FLAGS + ["-c", src, "-o", obj]
@@ -55,23 +59,29 @@ def _compile(src: str, extra=()) -> str:
     return obj
 
 
-def build(jobs: int | None = None, extra=(), verbose: bool = False) -> str:
+def build(jobs: int | None = None, extra=(), verbose: bool = False, lib: str = LIB, objdir: str = OBJDIR) -> str:
     """Compile every source and link the shared library; returns its path."""
-    os.makedirs(OBJDIR, exist_ok=True)
+    os.makedirs(objdir, exist_ok=True)
     srcs = sources()
     jobs = jobs or min(8, len(srcs))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, extra, objdir), srcs))
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
     _check_no_missing_kernels(tmp)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
+
+
+def build_stamps(jobs: int | None = None, verbose: bool = False) -> str:
+    """The phase/timeline-stamp build of the library (a separate file, objects under _build/stamps)."""
+    return build(jobs, extra=("-DASTR_PHASE_STAMPS=1",), verbose=verbose, lib=STAMPS_LIB,
+                 objdir=os.path.join(OBJDIR, "stamps"))
 
 
 def _check_no_missing_kernels(lib: str) -> None:
@@ -114,10 +124,13 @@ def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=None)
     ap.add_argument("--probes", action="store_true", help="also build the measurement programs in probes/")
+    ap.add_argument("--stamps", action="store_true", help="also build the phase/timeline-stamp library")
     args = ap.parse_args(argv)
     build(args.jobs, verbose=True)
     if args.probes:
         build_probes(verbose=True)
+    if args.stamps:
+        build_stamps(args.jobs, verbose=True)
 
 
 if __name__ == "__main__":

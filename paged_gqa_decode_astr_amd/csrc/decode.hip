@@ -66,6 +66,21 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 
+// Optional timeline stamps (built only with ASTR_PHASE_STAMPS=1, into a
+// separate library; the library as shipped has none of this code): thread 0
+// of each of the first kStampWgs split work groups records the constant
+// 100 MHz clock (s_memrealtime) at its start, once kv_indptr is staged, when
+// its first tile's loads are issued and at its end, its hardware CU and XCD
+// ids and its piece count.
+#ifndef ASTR_PHASE_STAMPS
+#define ASTR_PHASE_STAMPS 0
+#endif
+constexpr bool kStamps = ASTR_PHASE_STAMPS != 0;
+constexpr int kStampWgs = 4096;
+#if ASTR_PHASE_STAMPS
+__device__ unsigned long long g_decode_stamps[kStampWgs][8];
+#endif
+
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kTile = 16;       // keys per wavefront per tile (one MFMA column block)
@@ -214,6 +229,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(split_
   static_assert(G * D * sizeof(float) <= sizeof(sm_v[0]), "slot B (G x D floats) must fit a wavefront's V tile area");
   __shared__ int32_t sm_kv[kKvStage];                              // window of kv_indptr starting at kv_base
 
+  [[maybe_unused]] const unsigned long long stamp_start = kStamps ? __builtin_amdgcn_s_memrealtime() : 0;
   const int w = blockIdx.x;
   const int g = blockIdx.y;
   const int B = p.batch;
@@ -245,6 +261,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(split_
   const int64_t W = min((int64_t)p.num_splits, N);
   if (w >= W) return;  // uniform over the work group
 
+  [[maybe_unused]] const unsigned long long stamp_staged = kStamps ? __builtin_amdgcn_s_memrealtime() : 0;
+  [[maybe_unused]] unsigned long long stamp_first = 0;
   PieceTable pt;
   pt.e0 = (int)(((int64_t)w * N) / W);
   pt.e1 = (int)(((int64_t)(w + 1) * N) / W);
@@ -260,6 +278,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(split_
   } else {
     bnext = request_of(p.kv_indptr, B, pt.e0);
   }
+  [[maybe_unused]] const int stamp_b0 = bnext;
 
   // APPEND: requests bnext .. bnext + n_last - 1 have their last key in this
   // range (those with kv_indptr[b + 1] <= e1; the request holding e0 ends
@@ -440,6 +459,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(split_
       // (a work-group barrier orders the stores before the loads).
       if (first_window && n_last > 0) __syncthreads();   // uniform over the work group
       first_window = false;
+    }
+    if constexpr (kStamps) {
+      if (stamp_first == 0) stamp_first = __builtin_amdgcn_s_memrealtime();
     }
     Cursor c0;
     {
@@ -660,6 +682,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(split_
     }
     __syncthreads();
   }
+#if ASTR_PHASE_STAMPS
+  if (tid == 0) {
+    const int id = blockIdx.y * gridDim.x + blockIdx.x;
+    if (id < kStampWgs) {
+      unsigned long long* d = g_decode_stamps[id];
+      d[0] = stamp_start;
+      d[1] = stamp_staged;
+      d[2] = stamp_first;
+      d[3] = __builtin_amdgcn_s_memrealtime();
+      d[4] = __builtin_amdgcn_s_getreg(4 | (31 << 11));    // HW_ID: CU, shader array and engine of the wave
+      d[5] = __builtin_amdgcn_s_getreg(20 | (31 << 11));   // XCC_ID: the accelerator die
+      d[6] = (unsigned long long)(bnext - stamp_b0);      // pieces
+      d[7] = 1;
+    }
+  }
+#endif
 }
 
 // One work group per (request, kCombineHeads query heads) with
@@ -827,3 +865,20 @@ hipError_t launch_decode_split(const DecodeLaunch& p, hipStream_t s, const Timin
 hipError_t launch_decode_combine(const DecodeLaunch& p, hipStream_t s, const Timing& t) { ASTR_DECODE_CASES(launch_combine_t) }
 
 }  // namespace astr
+
+#if ASTR_PHASE_STAMPS
+// Timeline-stamp builds only: copy out or clear the split work groups'
+// records ([kStampWgs][8] unsigned 64-bit, work group id = y * grid_x + x:
+// start, kv_indptr staged, first tile issued, end (100 MHz clock), HW_ID,
+// XCC_ID, pieces, 1 when written).
+extern "C" int astr_debug_decode_stamps(void* host, size_t bytes) {
+  if (bytes < sizeof(astr::g_decode_stamps)) return (int)hipErrorInvalidValue;
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(astr::g_decode_stamps), sizeof(astr::g_decode_stamps));
+}
+extern "C" int astr_debug_decode_stamps_clear(void) {
+  void* ptr = nullptr;
+  hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(astr::g_decode_stamps));
+  if (e != hipSuccess) return (int)e;
+  return (int)hipMemset(ptr, 0, sizeof(astr::g_decode_stamps));
+}
+#endif

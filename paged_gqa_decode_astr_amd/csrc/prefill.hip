@@ -67,6 +67,22 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 
+// Optional phase stamps (built only with ASTR_PHASE_STAMPS=1, into a
+// separate library; the library as shipped has none of this code): every
+// wavefront of the first kStampWgs work groups adds up, per phase of the tile
+// loop, the shader-clock cycles (s_memtime) it spends -- issuing the next
+// tile's gather, S = K Q^T with the softmax, P.V, waiting for the gather, the
+// barrier -- and counts its tiles.
+#ifndef ASTR_PHASE_STAMPS
+#define ASTR_PHASE_STAMPS 0
+#endif
+constexpr bool kStamps = ASTR_PHASE_STAMPS != 0;
+constexpr int kStampWgs = 4096;
+constexpr int kStampPhases = 6;   // gather issue, S + softmax, P.V, gather wait, barrier, tiles
+#if ASTR_PHASE_STAMPS
+__device__ unsigned long long g_prefill_stamps[kStampWgs][8][kStampPhases];
+#endif
+
 constexpr int kRows = 128;       // (position, head) rows per work group
 // 16-row blocks per wavefront: two up to head_dim 128 (each K and V operand
 // read from LDS feeds two MFMAs), one at 256, where two blocks' accumulators
@@ -376,8 +392,20 @@ __global__ __launch_bounds__(prefill_threads<D>()) __attribute__((amdgpu_waves_p
 
   // Tiles wholly below the first row's causal limit run without mask code,
   // the remaining (diagonal) tiles with it.
+  [[maybe_unused]] unsigned long long ph[kStampPhases] = {0, 0, 0, 0, 0, 0};
+  auto stamp = [&]() __attribute__((always_inline)) -> unsigned long long {
+    if constexpr (kStamps) {
+      __builtin_amdgcn_sched_barrier(0);
+      const unsigned long long t = __builtin_amdgcn_s_memtime();
+      __builtin_amdgcn_sched_barrier(0);
+      return t;
+    } else {
+      return 0;
+    }
+  };
   auto tile = [&](auto masked, auto stage, int it) __attribute__((always_inline)) {
     {
+      [[maybe_unused]] const unsigned long long T0 = stamp();
       const int t0 = it * KT;
       const bool more = it + 1 < it_hi;   // uniform
       if (more) {
@@ -385,6 +413,7 @@ __global__ __launch_bounds__(prefill_threads<D>()) __attribute__((amdgpu_waves_p
         load_ids(t0 + 2 * KT);
         if constexpr (MASK) load_mask(t0 + KT, mnext);
       }
+      [[maybe_unused]] const unsigned long long T1 = stamp();
       const uint16_t* kt = decltype(stage)::value == 0 ? sK0 : sK1;
       const uint16_t* vt = decltype(stage)::value == 0 ? sV0 : sV1;
       const int swk = swz(l16);                               // K operand rows 16 tb + l16
@@ -503,6 +532,7 @@ __global__ __launch_bounds__(prefill_threads<D>()) __attribute__((amdgpu_waves_p
           dst[k2] = __builtin_bit_cast(bf16x8, both);
         }
       };
+      [[maybe_unused]] const unsigned long long T2 = stamp();
       bf16x8 va[2][2];
       vread(0, va[0]);
   #pragma unroll
@@ -515,7 +545,21 @@ __global__ __launch_bounds__(prefill_threads<D>()) __attribute__((amdgpu_waves_p
           for (int rb = 0; rb < kRB; ++rb) acc[rb][db] = mfma32k(va[db & 1][k2], pop[rb][k2], acc[rb][db]);
       }
 
-      stage_ready();   // the next stage is loaded; this one may be overwritten
+      if constexpr (kStamps) {
+        const unsigned long long T3 = stamp();
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        const unsigned long long T4 = stamp();
+        stage_ready();
+        const unsigned long long T5 = stamp();
+        ph[0] += T1 - T0;
+        ph[1] += T2 - T1;
+        ph[2] += T3 - T2;
+        ph[3] += T4 - T3;
+        ph[4] += T5 - T4;
+        ph[5] += 1;
+      } else {
+        stage_ready();   // the next stage is loaded; this one may be overwritten
+      }
       if constexpr (MASK) {
 #pragma unroll
         for (int rb = 0; rb < kRB; ++rb)
@@ -540,6 +584,11 @@ __global__ __launch_bounds__(prefill_threads<D>()) __attribute__((amdgpu_waves_p
   run_tiles(std::false_type{}, it_lo, it_plain);
   run_tiles(std::true_type{}, it_plain, it_hi);
 
+#if ASTR_PHASE_STAMPS
+  if (lane == 0 && blockIdx.x < kStampWgs) {
+    for (int i = 0; i < kStampPhases; ++i) g_prefill_stamps[blockIdx.x][wv][i] = ph[i];
+  }
+#endif
   // acc[rb][db][q] = O^T[d = 16 db + 4 kb + q][row 16 rb + l16], relative to mref.
   float ltot[kRB];
 #pragma unroll
@@ -692,3 +741,19 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t s, const Timing& t
 }
 
 }  // namespace astr
+
+#if ASTR_PHASE_STAMPS
+// Phase-stamp builds only: copy out or clear the per-wavefront phase cycles
+// ([kStampWgs][8][6] unsigned 64-bit: gather issue, S + softmax, P.V, gather
+// wait, barrier, tiles).
+extern "C" int astr_debug_prefill_stamps(void* host, size_t bytes) {
+  if (bytes < sizeof(astr::g_prefill_stamps)) return (int)hipErrorInvalidValue;
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(astr::g_prefill_stamps), sizeof(astr::g_prefill_stamps));
+}
+extern "C" int astr_debug_prefill_stamps_clear(void) {
+  void* ptr = nullptr;
+  hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(astr::g_prefill_stamps));
+  if (e != hipSuccess) return (int)e;
+  return (int)hipMemset(ptr, 0, sizeof(astr::g_prefill_stamps));
+}
+#endif

@@ -19,9 +19,20 @@ Subcommands:
             profiles/prefill_kernel_<config>_pmc.{json,md}.
   trace     runs bench.py under rocprofv3 --kernel-trace --stats and writes
             profiles/decode_<config>_kernel_trace.md.
+  prefill-phases
+            loads the phase-stamp build of the library (build --stamps), runs
+            one prefill call of <config> (default prefill_b8) with its plan and
+            writes the per-wavefront cycles of each tile-loop phase to
+            profiles/prefill_kernel_<config>_phases.{json,md}.
+  decode-timeline
+            loads the same build, runs --calls cold decode calls of <config>
+            and writes the split work groups' timeline (start, kv_indptr
+            staged, first tile, end; by kv head, XCD and piece count) to
+            profiles/decode_split_<config>_timeline.{json,md}.
 
 `pmc` and `trace` never touch the GPU themselves (rocprofv3 starts the
-profiled program as a child process).  Algorithmic byte counts live here too,
+profiled program as a child process); `prefill-phases` and `decode-timeline`
+run the kernels in this process.  Algorithmic byte counts live here too,
 so that bench.py and the summaries use one definition.
 """
 from __future__ import annotations
@@ -386,6 +397,174 @@ def _trace(args, bench_args):
     return 0
 
 
+# ----------------------------------------------------------------------------- stamped builds
+
+STAMP_WGS = 4096   # work groups whose stamps the kernels keep (kStampWgs in prefill.hip / decode.hip)
+
+
+def _stamps_lib():
+    import ctypes
+
+    from . import _lib, build
+    if not os.path.exists(build.STAMPS_LIB):
+        raise SystemExit(f"{build.STAMPS_LIB} is missing: python -m paged_gqa_decode_astr_amd.build --stamps")
+    lib = _lib.load_library(build.STAMPS_LIB)
+    for name in ("astr_debug_prefill_stamps", "astr_debug_decode_stamps"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+        clear = getattr(lib, name + "_clear")
+        clear.restype = ctypes.c_int
+        clear.argtypes = []
+    return lib
+
+
+def _write_summary(stem, rec, lines):
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(stem + ".json", "w") as fh:
+        json.dump(rec, fh, indent=1)
+    with open(stem + ".md", "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(json.dumps(rec), flush=True)
+
+
+def _prefill_phases(args):
+    import numpy as np
+    import torch
+
+    from . import tensors
+    from .workloads import make_inputs
+    lib = _stamps_lib()
+    inp = make_inputs(args.config, 0)
+    d = tensors.to_device(inp, "cuda")
+    o = torch.empty_like(d["q"])
+    ws = tensors.prefill_workspace(d)            # the library's own plan (None: whole tiles)
+    for _ in range(args.warmup):
+        tensors.run_prefill(d, o=o, workspace=ws)
+    torch.cuda.synchronize()
+    assert lib.astr_debug_prefill_stamps_clear() == 0
+    torch.cuda.synchronize()
+    tensors.run_prefill(d, o=o, workspace=ws)
+    torch.cuda.synchronize()
+    buf = np.zeros((STAMP_WGS, 8, 6), dtype=np.uint64)
+    assert lib.astr_debug_prefill_stamps(buf.ctypes.data, buf.nbytes) == 0
+    tiles = buf[:, :, 5].astype(np.float64)
+    wg_tiles = tiles.max(axis=1)
+    used = wg_tiles > 0
+    waves = tiles > 0
+    per_tile = buf[:, :, :5].astype(np.float64) / np.maximum(tiles, 1)[:, :, None]
+    names = ["gather_issue", "s_and_softmax", "pv", "gather_wait", "barrier"]
+    top = used & (wg_tiles >= np.percentile(wg_tiles[used], 90))
+    sel_top = waves & top[:, None]
+
+    def means(mask):
+        return {n: round(float(per_tile[..., i][mask].mean()), 1) for i, n in enumerate(names)}
+    rec = {"kernel": "prefill_kernel", "workload": args.config,
+           "command": f"python3 -m paged_gqa_decode_astr_amd.profiling prefill-phases --config {args.config} "
+                      f"--warmup {args.warmup}",
+           "sources": {pth: sources_digest_of(pth) for pth in PREFILL_SOURCES},
+           "work_groups": int(used.sum()), "max_key_tiles": int(wg_tiles.max()),
+           "cycles_per_tile_all": means(waves), "cycles_per_tile_longest_10pct": means(sel_top)}
+    rec["cycles_per_tile_all"]["total"] = round(sum(rec["cycles_per_tile_all"].values()), 1)
+    rec["cycles_per_tile_longest_10pct"]["total"] = round(sum(rec["cycles_per_tile_longest_10pct"].values()), 1)
+    lines = [f"# prefill_kernel phase cycles per 64-key tile, workload {args.config}", "",
+             f"Command: `{rec['command']}` (after `python -m paged_gqa_decode_astr_amd.build --stamps`).", "",
+             "The phase-stamp build of the library (`ASTR_PHASE_STAMPS=1`; the shipped kernels have none of "
+             "this code) adds up, per wavefront, the shader-clock cycles (`s_memtime`) of each phase of every "
+             "key tile: issuing the next tile's gather, S = K Q^T with mask and softmax, P.V, waiting for the "
+             "gather, the barrier. One call with the library's plan "
+             f"({rec['work_groups']} work groups, up to {rec['max_key_tiles']} key tiles each).", "",
+             "| phase | cycles per tile, all wavefronts | cycles per tile, the 10 % of work groups with the most tiles |",
+             "|---|---|---|"]
+    for n in names + ["total"]:
+        lines.append(f"| {n} | {rec['cycles_per_tile_all'][n]} | {rec['cycles_per_tile_longest_10pct'][n]} |")
+    _write_summary(os.path.join(PROFILES, f"prefill_kernel_{args.config}_phases"), rec, lines)
+    return 0
+
+
+def _decode_timeline(args):
+    import numpy as np
+    import torch
+
+    from . import _lib, tensors
+    lib = _stamps_lib()
+    sets = tensors.decode_sets(args.config, args.sets, "cuda", num_splits=args.num_splits)
+    torch.cuda.synchronize()
+    d0 = sets[0][1]
+    pargs, keep = _lib.make_args(d0["q"], d0["k_pool"], d0["v_pool"], d0["req_to_token"], d0["kv_indptr"],
+                                 d0["kv_indptr_host"], d0["o"], sm_scale=1.0,
+                                 req_to_token_stride=d0["req_to_token_stride"], num_splits=args.num_splits)
+    plan = _lib.astr_plan_decode(pargs, 0)
+    del keep
+    gx = plan.grid_x
+    for k in range(args.warmup):
+        tensors.decode_step(sets, k, num_splits=args.num_splits)
+    torch.cuda.synchronize()
+    stats = []
+    by_head, by_xcd, by_pieces = {}, {}, {}
+    for k in range(args.warmup, args.warmup + args.calls):
+        assert lib.astr_debug_decode_stamps_clear() == 0
+        torch.cuda.synchronize()
+        tensors.decode_step(sets, k, num_splits=args.num_splits)
+        torch.cuda.synchronize()
+        buf = np.zeros((STAMP_WGS, 8), dtype=np.uint64)
+        assert lib.astr_debug_decode_stamps(buf.ctypes.data, buf.nbytes) == 0
+        ids = np.nonzero(buf[:, 7])[0]
+        r = buf[ids].astype(np.float64)
+        t0 = r[:, 0].min()
+        start, staged, first, end = ((r[:, i] - t0) / 100.0 for i in range(4))   # 100 MHz clock -> us
+        loop = end - first
+        stats.append({"wgs": len(ids), "span": end.max(), "start_p50": np.median(start), "start_max": start.max(),
+                      "staged": np.median(staged - start), "setup": np.median(first - staged),
+                      "loop": np.percentile(loop, [10, 50, 90, 100]), "end": np.percentile(end, [10, 50, 90, 100])})
+        for key, dct in ((ids // gx, by_head), ((r[:, 5].astype(np.int64) & 0xF), by_xcd), (r[:, 6].astype(np.int64), by_pieces)):
+            for v in np.unique(key):
+                dct.setdefault(int(v), []).extend(loop[key == v].tolist())
+
+    def med(key):
+        return round(float(np.median([s_[key] for s_ in stats])), 2)
+
+    def medv(key):
+        return [round(float(x), 2) for x in np.median(np.array([s_[key] for s_ in stats]), axis=0)]
+    rec = {"kernel": "decode_split_kernel", "workload": args.config,
+           "command": f"python3 -m paged_gqa_decode_astr_amd.profiling decode-timeline --config {args.config} "
+                      f"--sets {args.sets} --warmup {args.warmup} --calls {args.calls}",
+           "sources": sources_digest(), "work_groups": int(stats[0]["wgs"]), "grid_x": gx, "calls": args.calls,
+           "span_us": med("span"), "start_us_p50": med("start_p50"), "start_us_max": med("start_max"),
+           "kv_indptr_staged_us": med("staged"), "setup_to_first_tile_us": med("setup"),
+           "loop_us_p10_p50_p90_max": medv("loop"), "end_us_p10_p50_p90_max": medv("end"),
+           "loop_us_by_kv_head": {h: round(float(np.mean(v)), 2) for h, v in sorted(by_head.items())},
+           "loop_us_by_xcd": {x: round(float(np.mean(v)), 2) for x, v in sorted(by_xcd.items())},
+           "loop_us_by_pieces": {n: round(float(np.mean(v)), 2) for n, v in sorted(by_pieces.items())}}
+    lines = [f"# decode_split_kernel work-group timeline, workload {args.config}", "",
+             f"Command: `{rec['command']}` (after `python -m paged_gqa_decode_astr_amd.build --stamps`).", "",
+             "The timeline-stamp build of the library (`ASTR_PHASE_STAMPS=1`; the shipped kernels have none of "
+             "this code) records, per split work group, the 100 MHz clock (`s_memrealtime`) at its start, once "
+             "kv_indptr is staged, when its first tile's loads are issued and at its end, with its XCD and piece "
+             f"count. Cold calls rotating over {args.sets} input sets; medians over {args.calls} calls; times in "
+             f"µs from the first work group's start. {rec['work_groups']} work groups "
+             f"(grid {gx} × kv heads, dispatched head by head).", "",
+             "| quantity | value |", "|---|---|",
+             f"| last work group ends (µs) | {rec['span_us']} |",
+             f"| work-group starts: median / last (µs) | {rec['start_us_p50']} / {rec['start_us_max']} |",
+             f"| kv_indptr staged after start (median µs) | {rec['kv_indptr_staged_us']} |",
+             f"| staged to first tile issued (median µs) | {rec['setup_to_first_tile_us']} |",
+             f"| tile loop p10 / p50 / p90 / max (µs) | {' / '.join(map(str, rec['loop_us_p10_p50_p90_max']))} |",
+             f"| work-group ends p10 / p50 / p90 / max (µs) | {' / '.join(map(str, rec['end_us_p10_p50_p90_max']))} |",
+             "", "Mean tile-loop time (µs):", "",
+             "| kv head | " + " | ".join(str(h) for h in rec["loop_us_by_kv_head"]) + " |",
+             "|---|" + "---|" * len(rec["loop_us_by_kv_head"]),
+             "| loop | " + " | ".join(str(v) for v in rec["loop_us_by_kv_head"].values()) + " |", "",
+             "| XCD | " + " | ".join(str(x) for x in rec["loop_us_by_xcd"]) + " |",
+             "|---|" + "---|" * len(rec["loop_us_by_xcd"]),
+             "| loop | " + " | ".join(str(v) for v in rec["loop_us_by_xcd"].values()) + " |", "",
+             "| pieces | " + " | ".join(str(n) for n in rec["loop_us_by_pieces"]) + " |",
+             "|---|" + "---|" * len(rec["loop_us_by_pieces"]),
+             "| loop | " + " | ".join(str(v) for v in rec["loop_us_by_pieces"].values()) + " |"]
+    _write_summary(os.path.join(PROFILES, f"decode_split_{args.config}_timeline"), rec, lines)
+    return 0
+
+
 def main(argv=None):
     argv = list(sys.argv[1:] if argv is None else argv)
     bench_args = []
@@ -393,7 +572,8 @@ def main(argv=None):
         i = argv.index("--")
         argv, bench_args = argv[:i], argv[i + 1:]
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("mode", choices=["workload", "pmc", "prefill-workload", "prefill-pmc", "trace"])
+    ap.add_argument("mode", choices=["workload", "pmc", "prefill-workload", "prefill-pmc", "trace", "prefill-phases",
+                                     "decode-timeline"])
     ap.add_argument("--config", default="decode_b32")
     ap.add_argument("--sets", type=int, default=4)
     ap.add_argument("--warmup", type=int, default=8)
@@ -416,6 +596,12 @@ def main(argv=None):
         if args.config == "decode_b32":
             args.config = "prefill_b8"
         return _prefill_pmc(args)
+    if args.mode == "prefill-phases":
+        if args.config == "decode_b32":
+            args.config = "prefill_b8"
+        return _prefill_phases(args)
+    if args.mode == "decode-timeline":
+        return _decode_timeline(args)
     # Default: the headline decode leg of bench.py (and its masked variant, a kernel of its own) only:
     # its other legs -- the other decode workloads, graph and append -- launch the same kernel at
     # other shapes, which would enter the kernel's average.
