@@ -17,8 +17,10 @@ Subcommands:
             counters (matrix-core busy cycles and bf16 MFMA operations, VALU and
             LDS activity, wave occupancy) and writes
             profiles/prefill_kernel_<config>_pmc.{json,md}.
-  trace     runs bench.py under rocprofv3 --kernel-trace --stats and writes
-            profiles/decode_<config>_kernel_trace.md.
+  trace     runs a decode workload's bench.py leg (or, for a prefill
+            workload, prefill-workload) under rocprofv3 --kernel-trace --stats
+            and writes profiles/decode_<config>_kernel_trace.md (or
+            profiles/prefill_<config>_kernel_trace.md).
   prefill-phases
             loads the phase-stamp build of the library (build --stamps), runs
             one prefill call of <config> (default prefill_b8) with its plan and
@@ -271,9 +273,10 @@ def _prefill_workload(args):
     d = tensors.to_device(inp, "cuda")
     o = torch.empty_like(d["q"])
     lse = torch.empty(d["q"].shape[0], d["q"].shape[1], dtype=torch.float32, device="cuda")
+    ws = tensors.prefill_workspace(d)   # zeroed once; every call leaves its counters at zero
     torch.cuda.synchronize()
     for _ in range(args.warmup + args.calls):
-        tensors.run_prefill(d, o=o, lse=lse)
+        tensors.run_prefill(d, o=o, lse=lse, workspace=ws)
     torch.cuda.synchronize()
     print(f"[prefill-workload] {args.config}: {args.warmup}+{args.calls} prefill calls", flush=True)
     return 0
@@ -364,10 +367,28 @@ def _prefill_pmc(args):
 
 
 def _trace(args, bench_args):
+    """Kernel trace of one workload: a decode workload through bench.py (its headline leg only, unless
+    bench arguments are given), a prefill workload through prefill-workload."""
     raw = os.path.abspath(args.raw)
     os.makedirs(raw, exist_ok=True)
-    bench_cmd = [sys.executable, os.path.join(ROOT, "bench.py")] + bench_args
-    cmd = ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d", raw, "-o", "run", "--"] + bench_cmd
+    prefill = args.config.startswith("prefill")
+    if prefill:
+        prog = ["-m", "paged_gqa_decode_astr_amd.profiling", "prefill-workload", "--config", args.config,
+                "--warmup", str(args.warmup), "--calls", str(args.calls)]
+        path = os.path.join(PROFILES, f"prefill_{args.config}_kernel_trace.md")
+        title = f"# Kernel trace of the prefill workload {args.config}\n\n"
+    else:
+        if not bench_args:
+            # The headline leg only (plus, at decode_b32, its masked variant, a kernel of its own):
+            # bench.py's other legs launch the same kernels at other shapes, which would enter
+            # the kernels' averages.
+            bench_args = ["--config", args.config, "--cpu-seconds", "0", "--no-graph", "--no-append", "--no-warm",
+                          "--no-configs", "--no-prefill"] + ([] if args.config == "decode_b32" else ["--no-masked"])
+        prog = [os.path.join(ROOT, "bench.py")] + bench_args
+        path = os.path.join(PROFILES, f"decode_{args.config}_kernel_trace.md")
+        title = f"# Kernel trace of the decode benchmark, workload {args.config}\n\n"
+    cmd = ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d", raw, "-o", "run", "--",
+           sys.executable] + prog
     _run_profiler(cmd, os.path.join(raw, "trace.log"), args.timeout)
     stats = glob.glob(os.path.join(raw, "**", "*kernel_stats.csv"), recursive=True)
     if not stats:
@@ -379,11 +400,11 @@ def _trace(args, bench_args):
         for line in fh:
             if line.startswith("{") and '"metric"' in line:
                 bench = json.loads(line)
-    shown = " ".join(shlex.quote(c) for c in ["python3", "bench.py"] + bench_args)
-    path = os.path.join(PROFILES, f"decode_{args.config}_kernel_trace.md")
+    shown = " ".join(shlex.quote(c) for c in ["python3"] + [os.path.relpath(c, ROOT) if c.startswith(ROOT) else c
+                                                             for c in prog])
     os.makedirs(PROFILES, exist_ok=True)
     with open(path, "w") as fh:
-        fh.write(f"# Kernel trace of the decode benchmark, workload {args.config}\n\n")
+        fh.write(title)
         fh.write("Command: `cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats --output-format csv "
                  f"-d <raw> -o run -- {shown}`\n\n")
         fh.write("| kernel | calls | average (us) | min (us) | max (us) | share of GPU time (%) |\n|---|---|---|---|---|---|\n")
@@ -602,11 +623,7 @@ def main(argv=None):
         return _prefill_phases(args)
     if args.mode == "decode-timeline":
         return _decode_timeline(args)
-    # Default: the headline decode leg of bench.py (and its masked variant, a kernel of its own) only:
-    # its other legs -- the other decode workloads, graph and append -- launch the same kernel at
-    # other shapes, which would enter the kernel's average.
-    return _trace(args, bench_args or ["--cpu-seconds", "0", "--no-graph", "--no-append", "--no-warm",
-                                       "--no-configs", "--no-prefill"])
+    return _trace(args, bench_args)
 
 
 if __name__ == "__main__":
