@@ -244,6 +244,25 @@ int32_t combine_groups(const astr_paged_args* a, int64_t total_keys, int64_t wh)
   return (int32_t)(g < 1 ? 1 : (g > 8 ? 8 : g));
 }
 
+// Head blocks (of 64 * 4 / head_dim query heads each) per combine work group.
+// Large grids launch faster as fewer, larger work groups (measured on MI355X,
+// B = 256 and 32 query heads: 8.2 -> 5.6 us from 4096 work groups of one
+// block to 1024 of four), small ones lose the parallelism (B = 1: 6.3 ->
+// 8.2 us), so blocks are merged only while the grid keeps at least
+// kCombineMinGroups work groups, and while groups x blocks fit in 1024
+// threads.  The count changes which work group computes a head, not how.
+constexpr int32_t kCombineMaxHeadBlocks = 4;
+constexpr int64_t kCombineMinGroups = 1024;
+int32_t combine_head_blocks(const astr_paged_args* a, int32_t groups) {
+  const int32_t per_block = 64 * 4 / a->head_dim;
+  const int64_t blocks = (a->num_qo_heads + per_block - 1) / per_block;
+  int32_t n = 1;
+  while (n < kCombineMaxHeadBlocks && 2 * n * groups <= 16 &&
+         (int64_t)a->batch * ceil_div(blocks, 2 * (int64_t)n) >= kCombineMinGroups)
+    n *= 2;
+  return n;
+}
+
 int plan_decode_impl(const astr_paged_args* a, int64_t total_keys, int32_t num_cus, astr_decode_plan* out) {
   int64_t wh;
   if (a->num_splits > 0) {
@@ -531,6 +550,7 @@ int astr::decode_impl(const astr_paged_args* a, const astr_new_kv* nkv, void* wo
   p.num_splits = plan.num_splits;
   p.num_partials = plan.num_partials;
   p.combine_groups = combine_groups(a, total, plan.num_splits);
+  p.combine_head_blocks = combine_head_blocks(a, p.combine_groups);
   p.o_part = static_cast<float*>(workspace);
   p.ml_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                        align256((int64_t)a->num_qo_heads * plan.num_partials * a->head_dim * 4));

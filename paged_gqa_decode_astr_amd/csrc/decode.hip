@@ -700,35 +700,42 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(split_
 #endif
 }
 
-// One work group per (request, kCombineHeads query heads) with
-// combine_groups groups of 64 threads (the host picks the group count from
-// the longest request's piece count; any count gives the same result up to
-// rounding order).  Thread t of a group owns four consecutive output
-// elements of one head (float4 loads) and folds pieces r, r + groups, ... of
-// the request, w_first..w_last (r = its group), into (M, den, num) with an
-// online log-sum-exp merge, kBatch pieces at a time so that their loads are
-// in flight together.  The groups then merge through LDS in group order, and
-// group 0 writes O (bf16, round to nearest even) and lse = M + ln(den).
+// One work group per (request, combine_head_blocks blocks of kHeads query
+// heads), each block with combine_groups groups of 64 threads (the host picks
+// the group count from the longest request's piece count, and as many head
+// blocks as fit in 1024 threads, at most 4: fewer, larger work groups launch
+// faster; any counts give the same result up to rounding order, and the
+// head-block count none at all).  Thread t of a group owns four consecutive
+// output elements of one head (float4 loads) and folds pieces r, r + groups,
+// ... of the request, w_first..w_last (r = its group), into (M, den, num)
+// with an online log-sum-exp merge, kBatch pieces at a time so that their
+// loads are in flight together.  The groups of a block then merge through
+// LDS in group order, and group 0 writes O (bf16, round to nearest even) and
+// lse = M + ln(den).
 constexpr int kBatch = 8;
 constexpr int kMaxCombineGroups = 8;
 constexpr int kCombineGroupThreads = kWave;
+constexpr int kMaxCombineThreads = 1024;
+// LDS slots for the groups r > 0 of all head blocks: groups x blocks <= 16.
+constexpr int kCombineSlots = kMaxCombineThreads / kCombineGroupThreads - 1;
 
 template <int D>
 struct CombineShape {
-  static constexpr int kHeads = kCombineGroupThreads * 4 / D;   // query heads per work group
+  static constexpr int kHeads = kCombineGroupThreads * 4 / D;   // query heads per head block
 };
 
 template <int D, int G>
-__global__ __launch_bounds__(kCombineGroupThreads * kMaxCombineGroups) void decode_combine_kernel(const DecodeLaunch p) {
+__global__ __launch_bounds__(kMaxCombineThreads) void decode_combine_kernel(const DecodeLaunch p) {
   constexpr int HP = CombineShape<D>::kHeads;
-  __shared__ float4 s_num[kMaxCombineGroups - 1][kCombineGroupThreads];
-  __shared__ float s_m[kMaxCombineGroups - 1][kCombineGroupThreads];
-  __shared__ float s_den[kMaxCombineGroups - 1][kCombineGroupThreads];
+  __shared__ float4 s_num[kCombineSlots][kCombineGroupThreads];
+  __shared__ float s_m[kCombineSlots][kCombineGroupThreads];
+  __shared__ float s_den[kCombineSlots][kCombineGroupThreads];
   const int b = blockIdx.x;
   const int t = threadIdx.x % kCombineGroupThreads;
-  const int grp = threadIdx.x / kCombineGroupThreads;
-  const int ngrp = blockDim.x / kCombineGroupThreads;
-  const int h = blockIdx.y * HP + t / (D / 4);
+  const int ngrp = p.combine_groups;
+  const int grp = (threadIdx.x / kCombineGroupThreads) % ngrp;
+  const int hb = threadIdx.x / (kCombineGroupThreads * ngrp);
+  const int h = (blockIdx.y * p.combine_head_blocks + hb) * HP + t / (D / 4);
   const int d4 = 4 * (t % (D / 4));
   const bool live = h < p.num_qo_heads;
   const int hc = live ? h : p.num_qo_heads - 1;   // idle threads read a valid row
@@ -779,20 +786,21 @@ __global__ __launch_bounds__(kCombineGroupThreads * kMaxCombineGroups) void deco
     M = Mb;
   }
   if (ngrp > 1) {
+    const int slot0 = hb * (ngrp - 1) - 1;   // slot of group r of this head block: slot0 + r
     if (grp > 0) {
-      s_num[grp - 1][t] = num;
-      s_m[grp - 1][t] = M;
-      s_den[grp - 1][t] = den;
+      s_num[slot0 + grp][t] = num;
+      s_m[slot0 + grp][t] = M;
+      s_den[slot0 + grp][t] = den;
     }
     __syncthreads();
     if (grp > 0) return;
-    for (int k = 0; k < ngrp - 1; ++k) {
-      const float mk = s_m[k][t];
+    for (int k = 1; k < ngrp; ++k) {
+      const float mk = s_m[slot0 + k][t];
       if (mk == -INFINITY) continue;   // group had no piece
       const float Mn = fmaxf(M, mk);
       const float a = M == -INFINITY ? 0.f : expf(M - Mn), c = expf(mk - Mn);   // M = -inf: group 0 saw no visible key
-      const float4 nk = s_num[k][t];
-      den = den * a + s_den[k][t] * c;
+      const float4 nk = s_num[slot0 + k][t];
+      den = den * a + s_den[slot0 + k][t] * c;
       num.x = num.x * a + nk.x * c;
       num.y = num.y * a + nk.y * c;
       num.z = num.z * a + nk.z * c;
@@ -828,8 +836,13 @@ hipError_t launch_split_t(const DecodeLaunch& p, hipStream_t s, const Timing& t)
 template <int D, int G>
 hipError_t launch_combine_t(const DecodeLaunch& p, hipStream_t s, const Timing& t) {
   constexpr int HP = CombineShape<D>::kHeads;
-  const dim3 grid(p.batch, (p.num_qo_heads + HP - 1) / HP, 1);
-  return launch_kernel(decode_combine_kernel<D, G>, grid, dim3(kCombineGroupThreads * p.combine_groups), s, t, p);
+  const int blocks = (p.num_qo_heads + HP - 1) / HP;
+  const int nhb = p.combine_head_blocks;
+  if (p.combine_groups < 1 || p.combine_groups > kMaxCombineGroups || nhb < 1 ||
+      p.combine_groups * nhb * kCombineGroupThreads > kMaxCombineThreads)
+    return hipErrorInvalidConfiguration;
+  const dim3 grid(p.batch, (blocks + nhb - 1) / nhb, 1);
+  return launch_kernel(decode_combine_kernel<D, G>, grid, dim3(kCombineGroupThreads * p.combine_groups * nhb), s, t, p);
 }
 
 #define ASTR_DECODE_CASES(FN)                       \

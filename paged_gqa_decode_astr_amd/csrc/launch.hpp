@@ -34,7 +34,8 @@ struct DecodeLaunch {
   uint32_t pool_range;   // off32: (num_slots - 1) * kv_stride_slot * 2 + head_dim * 2
   int32_t num_splits;    // Wh: work groups per kv head (grid.x)
   int32_t num_partials;  // P = Wh + B - 1 slots per query head
-  int32_t combine_groups;  // thread groups of the combine kernel (1..8)
+  int32_t combine_groups;  // thread groups of the combine kernel per head block (1..8)
+  int32_t combine_head_blocks;  // head blocks per combine work group (groups x blocks <= 16)
   float* o_part;         // [Hq][P][D]
   float* ml_part;        // [Hq][P][2]
   // Fused KV append (decode_append): the new token of request b is its last
