@@ -247,7 +247,11 @@ typedef struct astr_prefill_plan {
 #define ASTR_WORKSPACE_COUNTER_BYTES 32768
 
 /* Host-only prefill plan (validates a first; no HIP call unless num_cus <= 0,
- * which asks the current device's CU count).  Returns astr_status. */
+ * which asks the current device's CU count).  [extension @6f67ba8], the
+ * commit renaming the prefill kernels with _split_q / _mma suffixes (query
+ * tiles split over work groups, matrix-core products); the pages give no
+ * rule for the tiling, the one above is this library's.  Returns
+ * astr_status. */
 int astr_plan_prefill(const astr_paged_args* a, int32_t num_cus, astr_prefill_plan* out);
 
 /* Ragged paged prefill with causal offset seq_len - q_len per request
@@ -295,7 +299,9 @@ typedef struct astr_new_kv {
  * astr_status; on error nothing is enqueued. */
 int astr_kv_append(const astr_paged_args* a, const astr_new_kv* nkv, void* stream);
 
-/* Fused KV append + paged decode, one launch fewer than astr_kv_append
+/* Fused KV append + paged decode ([attention_backend.py @47b3ed4], the commit
+ * sharing one helper that writes the step's new K/V into the cache and then
+ * gathers the request's keys), one launch fewer than astr_kv_append
  * followed by astr_paged_decode, with the same result bit for bit (the same
  * kernels' arithmetic on the same values).  The new token of request b is
  * its last position L_b - 1 (kv_indptr counts it); its K/V row for kv head g
