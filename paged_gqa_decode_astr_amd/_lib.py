@@ -136,20 +136,22 @@ def _check(status: int):
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
 
 
 def _host_i32(x):
     """Host int32 copy of an index array (numpy or CPU tensor); kept alive by the caller."""
     if x is None:
         return None
+    if isinstance(x, np.ndarray) and x.dtype == np.int32 and x.flags.c_contiguous:
+        return x
     if hasattr(x, "detach"):
         x = x.detach().cpu().numpy()
     return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
 
 
 def _np_ptr(a):
-    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+    return None if a is None else a.ctypes.data
 
 
 def make_args(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host, o, *, sm_scale,
@@ -161,56 +163,52 @@ def make_args(q, k_pool, v_pool, req_to_token, kv_indptr, kv_indptr_host, o, *, 
     contiguous last dimension; nonzero = visible."""
     import torch
 
-    for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool), ("o", o)):
-        if t.dtype != torch.bfloat16:
+    bf16, i32 = torch.bfloat16, torch.int32
+    qs, ks, vs, os_ = q.stride(), k_pool.stride(), v_pool.stride(), o.stride()
+    for name, t, st in (("q", q, qs), ("k_pool", k_pool, ks), ("v_pool", v_pool, vs), ("o", o, os_)):
+        if t.dtype != bf16:
             raise TypeError(f"{name} must be bfloat16 (got {t.dtype})")
-        if t.dim() != 3 or t.stride(2) != 1:
+        if len(st) != 3 or st[2] != 1:
             raise ValueError(f"{name} must be 3-D with a contiguous last dimension")
     for name, t in (("req_to_token", req_to_token), ("kv_indptr", kv_indptr), ("qo_indptr", qo_indptr)):
-        if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
+        if t is not None and (t.dtype != i32 or not t.is_contiguous()):
             raise TypeError(f"{name} must be a contiguous int32 tensor")
-    if lse is not None and (lse.dtype != torch.float32 or lse.dim() != 2 or lse.stride(1) != 1):
-        raise TypeError("lse must be a 2-D float32 tensor with contiguous last dimension")
+    lse_stride = 0
+    if lse is not None:
+        ls = lse.stride()
+        if lse.dtype != torch.float32 or len(ls) != 2 or ls[1] != 1:
+            raise TypeError("lse must be a 2-D float32 tensor with contiguous last dimension")
+        lse_stride = ls[0]
+    if ks != vs or k_pool.shape != v_pool.shape:
+        raise ValueError("k_pool and v_pool must have the same shape and strides")
     kvh = _host_i32(kv_indptr_host)
     qoh = _host_i32(qo_indptr_host)
-    a = PagedArgs()
-    a.batch = kv_indptr.numel() - 1
-    a.num_qo_heads = q.shape[1]
-    a.num_kv_heads = k_pool.shape[1]
-    a.head_dim = q.shape[2]
-    a.sm_scale = float(sm_scale)
-    a.q = _ptr(q)
-    a.q_stride_tok, a.q_stride_head = q.stride(0), q.stride(1)
-    a.o = _ptr(o)
-    a.o_stride_tok, a.o_stride_head = o.stride(0), o.stride(1)
-    a.lse = _ptr(lse)
-    a.lse_stride_tok = lse.stride(0) if lse is not None else 0
-    a.k_pool = _ptr(k_pool)
-    a.v_pool = _ptr(v_pool)
-    if k_pool.stride() != v_pool.stride() or k_pool.shape != v_pool.shape:
-        raise ValueError("k_pool and v_pool must have the same shape and strides")
-    a.kv_stride_slot, a.kv_stride_head = k_pool.stride(0), k_pool.stride(1)
-    a.num_slots = k_pool.shape[0]
-    a.req_to_token = _ptr(req_to_token)
-    a.req_to_token_stride = int(req_to_token_stride)
-    a.kv_indptr = _ptr(kv_indptr)
-    a.kv_indptr_host = _np_ptr(kvh)
-    a.qo_indptr = _ptr(qo_indptr)
-    a.qo_indptr_host = _np_ptr(qoh)
-    a.num_splits = int(num_splits)
-    a.max_q_len = int(max_q_len)
-    a.non_causal = 1 if non_causal else 0
-    a.page_size = int(page_size)
+    mask_ptr, mask_req, mask_row = None, 0, 0
     if mask is not None:
         if mask.dtype not in (torch.uint8, torch.bool) or mask.dim() not in (2, 3) or mask.stride(-1) != 1:
             raise TypeError("mask must be a 2-D or 3-D uint8/bool tensor with a contiguous last dimension")
-        a.mask = _ptr(mask)
-        a.mask_stride_req = mask.stride(0)
-        a.mask_stride_row = mask.stride(1) if mask.dim() == 3 else 0
-    ev = None
+        mask_ptr = mask.data_ptr()
+        mask_req = mask.stride(0)
+        mask_row = mask.stride(1) if mask.dim() == 3 else 0
+    ev, ev_ptr = None, None
     if timing_events is not None:
         ev = (ctypes.c_void_p * len(timing_events))(*[None if e is None else e.cuda_event for e in timing_events])
-        a.timing_events = ctypes.cast(ev, ctypes.c_void_p)
+        ev_ptr = ctypes.addressof(ev)
+    qshape = q.shape
+    a = PagedArgs(
+        batch=kv_indptr.numel() - 1, num_qo_heads=qshape[1], num_kv_heads=k_pool.shape[1], head_dim=qshape[2],
+        sm_scale=float(sm_scale),
+        q=q.data_ptr(), q_stride_tok=qs[0], q_stride_head=qs[1],
+        o=o.data_ptr(), o_stride_tok=os_[0], o_stride_head=os_[1],
+        lse=_ptr(lse), lse_stride_tok=lse_stride,
+        k_pool=k_pool.data_ptr(), v_pool=v_pool.data_ptr(),
+        kv_stride_slot=ks[0], kv_stride_head=ks[1], num_slots=k_pool.shape[0],
+        req_to_token=req_to_token.data_ptr(), req_to_token_stride=int(req_to_token_stride),
+        kv_indptr=kv_indptr.data_ptr(), kv_indptr_host=_np_ptr(kvh),
+        qo_indptr=_ptr(qo_indptr), qo_indptr_host=_np_ptr(qoh),
+        num_splits=int(num_splits), max_q_len=int(max_q_len), timing_events=ev_ptr,
+        non_causal=1 if non_causal else 0, mask=mask_ptr, mask_stride_req=mask_req, mask_stride_row=mask_row,
+        page_size=int(page_size))
     return a, (kvh, qoh, ev)
 
 
