@@ -702,10 +702,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(split_
 
 // One work group per (request, combine_head_blocks blocks of kHeads query
 // heads), each block with combine_groups groups of 64 threads (the host picks
-// the group count from the longest request's piece count, and as many head
-// blocks as fit in 1024 threads, at most 4: fewer, larger work groups launch
-// faster; any counts give the same result up to rounding order, and the
-// head-block count none at all).  Thread t of a group owns four consecutive
+// the group count from the longest request's piece count, and merges up to 4
+// head blocks into one work group only for large grids, which launch faster
+// as fewer, larger work groups; any group count gives the same result up to
+// rounding order, the head-block count does not change it at all).  Thread t of a group owns four consecutive
 // output elements of one head (float4 loads) and folds pieces r, r + groups,
 // ... of the request, w_first..w_last (r = its group), into (M, den, num)
 // with an online log-sum-exp merge, kBatch pieces at a time so that their
