@@ -52,6 +52,21 @@ def test_decode_group_and_head_dim_variants(Hq, Hkv, D):
         assert_close(lse, ref_lse, f"variant ns={ns} lse", atol=1e-3, rtol=1e-4)
 
 
+@pytest.mark.parametrize("D", [128, 64])
+def test_decode_combine_head_blocks_with_several_groups(D):
+    """256 short requests and one long one: the combine's grid is large enough for several head
+    blocks per work group (4 at head_dim 128, 2 at 64) and the long request spans more than 8
+    pieces, so each block also has several thread groups merging through their own LDS slots."""
+    seq = np.full(256, 60)
+    seq[101] = 6000
+    inp = build_paged_inputs(seq, 32, 8, D, 1 << 15, seed=D + 7)
+    announce(f"decode combine head blocks D={D} B=256 N={int(seq.sum())}")
+    o, lse, _, _ = _decode(inp)
+    ref_o, ref_lse = oracle_of(inp)
+    assert_close(o, ref_o, f"combine head blocks D={D} O")
+    assert_close(lse, ref_lse, f"combine head blocks D={D} lse", atol=1e-3, rtol=1e-4)
+
+
 def test_decode_tile_boundary_lengths():
     seq = np.array([1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 511, 512, 513])
     inp = build_paged_inputs(seq, 32, 8, 128, 8192, seed=99)
